@@ -1,0 +1,213 @@
+"""Plain fp64 attention, written from the definitions on the source pages.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Deliberately slow and
+obvious: scores are materialised (in row blocks, to bound memory), masked,
+soft-maxed and multiplied by V.  No tiling, fusion or reordering beyond what
+the definitions state.  Inputs are numpy float64 arrays (the exact upcast of
+the bf16/f32 tensors the GPU receives).
+
+Sources (cited by page title and section):
+  [FA]    "flash-attention与TensorRT-LLM集成：大语言模型推理优化",
+          sections "背景与痛点分析" and "FlashAttention工作原理": FlashAttention
+          is an *exact* attention computed IO-aware, so its result is the plain
+          softmax(scale * Q K^T) V.
+  [GQA]   "TensorRT对Grouped Query Attention的支持进展", sub-sections
+          "技术演进背景" (query heads are split into groups; each group shares
+          one K/V head) and "图优化与算子融合" (the repeat_kv plugin repeats
+          each K/V head for the query heads of its group).
+  [KV]    "LLM推理优化技术综述：KVCache、PageAttention、FlashAttention、MQA、GQA",
+          parts on the autoregressive KV cache and PageAttention (a block table
+          maps a sequence's contiguous logical blocks to non-contiguous
+          physical blocks), and "TensorRT-LLM：大模型推理加速的工业级引擎",
+          PagedAttention section.
+  [BLASST] "高效部署稀疏注意力加速方案：BLASST方法详解与实践指南", section
+          "架构与组件": a running maximum of the attention scores from the
+          blockwise online softmax, a threshold lambda deciding whether a
+          block matters, and skipping exp, the V load and the matmul for
+          blocks that do not.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * layout [B, H, S, D]; query head h reads K/V head h // (Hq // Hkv)
+    (contiguous groups, the repeat_kv reading of [GQA]);
+  * causal: key j visible to query i iff j <= i (equal query/key lengths);
+  * LSE = natural log of sum_j exp(s_ij) over visible keys, s including scale;
+  * decode: the single new query sees all L cached tokens (no mask);
+  * block skip: whole T x T tiles per query head, ascending key-tile order,
+    strict test (tile row max) - (running max) < ln(lambda), a tile skipped
+    only when every one of its rows passes the test.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip"]
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """[GQA]: query heads form Hkv contiguous groups of Hq/Hkv heads; group g
+    shares K/V head g (each K/V head repeated Hq/Hkv times in a row)."""
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def _softmax_rows(s: np.ndarray):
+    """Row softmax of a score block whose masked entries are -inf.
+
+    Returns (P, lse) with P = exp(s - lse) and lse = ln sum_j exp(s_ij);
+    rows with no visible entry get P = 0 and lse = -inf.
+    """
+    m = np.max(s, axis=1, keepdims=True)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe)
+    z = np.sum(e, axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(empty, 0.0, e / np.where(z == 0, 1.0, z))
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(z == 0, 1.0, z)))
+    return p, lse[:, 0]
+
+
+def ref_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
+                scale: float, rows: Optional[Sequence[int]] = None,
+                row_block: int = 1024):
+    """Exact attention [FA] with GQA head sharing [GQA].
+
+    q: [B, Hq, S, D], k/v: [B, Hkv, S, D] float64.
+    rows: optional query positions to evaluate (every (b, h) uses the same
+    positions); default all S positions.
+    Returns (O [B, Hq, R, D], LSE [B, Hq, R]) in float64.
+    For each (b, h) with g = kv_head_of(h): s_ij = scale * <q_i, k_j>;
+    keys with j > i are masked when causal; P = softmax over visible keys;
+    O_i = sum_j P_ij v_j; LSE_i = ln sum_j exp(s_ij).
+    """
+    B, Hq, S, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    assert (Bk, Dk) == (B, D) and v.shape == k.shape
+    assert Sk == S, "query and key lengths are equal in prefill"
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    out = np.zeros((B, Hq, R, D), dtype=np.float64)
+    lse = np.zeros((B, Hq, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            kg, vg = k[b, g], v[b, g]
+            for r0 in range(0, R, row_block):
+                ri = rows[r0:r0 + row_block]
+                s = scale * (q[b, h, ri, :] @ kg.T)            # [rb, S]
+                if causal:
+                    s = np.where(np.arange(S)[None, :] <= ri[:, None], s, -np.inf)
+                p, l = _softmax_rows(s)
+                out[b, h, r0:r0 + row_block] = p @ vg
+                lse[b, h, r0:r0 + row_block] = l
+    return out, lse
+
+
+def ref_decode_paged(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                     block_table: np.ndarray, seq_lens: np.ndarray,
+                     block_size: int, scale: float):
+    """Decode attention over a paged KV cache [KV].
+
+    q: [N, Hq, D]; k_pool/v_pool: [NB, Hkv, block_size, D]; block_table:
+    [N, max_blocks] (entry j = physical block holding logical block j);
+    seq_lens: [N].  Cached token t of sequence n lives in physical block
+    block_table[n, t // block_size], slot t % block_size.  The new query sees
+    all L = seq_lens[n] cached tokens.  Returns (O [N, Hq, D], LSE [N, Hq]);
+    a sequence with L = 0 gets O = 0, LSE = -inf.
+    """
+    N, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_pool.shape
+    assert bs == block_size and Dk == D
+    out = np.zeros((N, Hq, D), dtype=np.float64)
+    lse = np.full((N, Hq), -np.inf, dtype=np.float64)
+    for n in range(N):
+        L = int(seq_lens[n])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        phys = block_table[n, t // block_size].astype(np.int64)
+        if np.any(phys < 0) or np.any(phys >= NB):
+            raise ValueError(f"sequence {n}: block table entry out of range")
+        slot = t % block_size
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            kn = k_pool[phys, g, slot, :]                     # [L, D] logical order
+            vn = v_pool[phys, g, slot, :]
+            s = scale * (kn @ q[n, h])                         # [L]
+            p, l = _softmax_rows(s[None, :])
+            out[n, h] = p[0] @ vn
+            lse[n, h] = l[0]
+    return out, lse
+
+
+def ref_blockskip(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
+                  lam: float, tile: int, qtiles: Optional[Sequence[int]] = None):
+    """Causal attention with BLASST block skipping [BLASST].
+
+    The kernel walks key tiles kt = 0, 1, ..., qt in ascending order for each
+    query tile qt (tile x tile blocks per query head) and keeps the running
+    row maximum m of the scaled scores.  For tile kt it forms the tile row
+    maxima tm_r (-inf where row r sees no key of the tile) and calls row r
+    negligible iff tm_r = -inf, or m_r > -inf and tm_r - m_r < ln(lam).  The
+    tile is skipped when all its rows are negligible: its exp, V load and P.V
+    are left out.  Because a skipped tile has tm_r < m_r for every row (ln lam
+    < 0), folding it into the maximum changes nothing, so the running max
+    before tile kt equals the plain prefix maximum over ALL tiles kt' < kt;
+    that is what is evaluated here.
+
+    Returns (O [B,Hq,R,D], LSE [B,Hq,R], skip [B,Hq,nQ,nK] bool,
+    gap [B,Hq,nQ,nK] float64) for the chosen query tiles (default: all),
+    where R = rows of those tiles, skip[...,i,kt] refers to qtiles[i], and
+    gap = max_r (tm_r - m_r) (+inf at kt = 0, -inf where kt > qt).
+    """
+    if not (0.0 < lam < 1.0):
+        raise ValueError("lambda must lie in (0, 1)")
+    B, Hq, S, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    assert Sk == S
+    nT = (S + tile - 1) // tile
+    qtiles = np.arange(nT) if qtiles is None else np.asarray(qtiles, dtype=np.int64)
+    ln_lam = math.log(lam)
+    row_list = [np.arange(qt * tile, min(S, (qt + 1) * tile)) for qt in qtiles]
+    R = sum(len(r) for r in row_list)
+    out = np.zeros((B, Hq, R, D))
+    lse = np.zeros((B, Hq, R))
+    skip = np.zeros((B, Hq, len(qtiles), nT), dtype=bool)
+    gap = np.full((B, Hq, len(qtiles), nT), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            kg, vg = k[b, g], v[b, g]
+            r_out = 0
+            for i, qt in enumerate(qtiles):
+                ri = row_list[i]
+                s = scale * (q[b, h, ri, :] @ kg.T)                     # [T, S]
+                vis = np.arange(S)[None, :] <= ri[:, None]
+                s = np.where(vis, s, -np.inf)
+                # tile row maxima tm[r, kt], kt = 0..nT-1
+                tm = np.full((len(ri), nT), -np.inf)
+                for kt in range(int(qt) + 1):
+                    tm[:, kt] = np.max(s[:, kt * tile:(kt + 1) * tile], axis=1)
+                for kt in range(int(qt) + 1):
+                    if kt == 0:
+                        m_prev = np.full(len(ri), -np.inf)
+                    else:
+                        m_prev = np.max(tm[:, :kt], axis=1)
+                    with np.errstate(invalid="ignore"):
+                        d = tm[:, kt] - m_prev
+                    neg = np.isneginf(tm[:, kt]) | (np.isfinite(m_prev) & (d < ln_lam))
+                    skip[b, h, i, kt] = bool(np.all(neg))
+                    gap[b, h, i, kt] = np.inf if kt == 0 else float(np.max(d))
+                keep = np.ones_like(vis)
+                for kt in np.nonzero(skip[b, h, i])[0]:
+                    keep[:, kt * tile:(kt + 1) * tile] = False
+                s = np.where(keep, s, -np.inf)
+                p, l = _softmax_rows(s)
+                out[b, h, r_out:r_out + len(ri)] = p @ vg
+                lse[b, h, r_out:r_out + len(ri)] = l
+                r_out += len(ri)
+    return out, lse, skip, gap

@@ -1,0 +1,335 @@
+"""Pins for the fp64 oracle: hand-derived worked examples, closed forms,
+invariants, an independent library routine and an independent sequential
+formulation of block skipping.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref_prefill, ref_decode_paged, ref_blockskip, kv_head_of
+from workloads import decode_inputs, upcast_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- worked examples
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_golden_causal_ln_weights(causal):
+    g = _golden("causal_ln_weights.json")
+    q = np.array(g["q"])[None, None]                       # [1,1,3,2]
+    k = np.array([[math.log(a), 0.0] for a in g["k_log_args"]])[None, None]
+    v = np.array(g["v"])[None, None]
+    o, lse = ref_prefill(q, k, v, causal=causal, scale=g["scale"])
+    exp = g["causal" if causal else "noncausal"]
+    np.testing.assert_allclose(o[0, 0], np.array(exp["o"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.log(exp["lse_log_args"]), rtol=0, atol=1e-12)
+
+
+def test_golden_gqa_two_groups():
+    g = _golden("gqa_two_groups.json")
+    Hq, Hkv, S = 4, 2, 2
+    q = np.zeros((1, Hq, S, 1))
+    for h, val in enumerate(g["q_heads"]):
+        q[0, h, :, 0] = val
+    k = np.log(np.array(g["k_heads_log_args"], dtype=np.float64))[None, :, :, None]
+    v = np.array(g["v_heads"])[None, :, :, None]
+    o, lse = ref_prefill(q, k, v, causal=False, scale=1.0)
+    for h in range(Hq):
+        np.testing.assert_allclose(o[0, h, :, 0], g["o_heads"][h], atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], math.log(g["lse_heads_log_args"][h]), atol=1e-12)
+
+
+def test_golden_blockskip_sink():
+    g = _golden("blockskip_sink.json")
+    T = g["tile"]
+    k = np.array(g["k"])[None, None, :, None]
+    v = np.array(g["v"])[None, None, :, None]
+    q = np.ones((1, 1, 4, 1))
+    v0, v1, v2, v3 = g["v"]
+    for case in g["cases"]:
+        o, lse, skip, gap = ref_blockskip(q, k, v, scale=1.0, lam=case["lam"], tile=T)
+        assert bool(skip[0, 0, 1, 1]) == case["skip_q1_k1"]
+        assert not skip[0, 0, :, 0].any()
+        np.testing.assert_allclose(gap[0, 0, 1, 1], -10.0, atol=1e-12)
+        e = math.exp(10.0)
+        if case["skip_q1_k1"]:
+            exp_o = [(v0 + v1) / 2] * 2
+            exp_l = [10 + math.log(2)] * 2
+        else:
+            exp_o = [(e * (v0 + v1) + v2) / (2 * e + 1), (e * (v0 + v1) + v2 + v3) / (2 * e + 2)]
+            exp_l = [math.log(2 * e + 1), math.log(2 * e + 2)]
+        np.testing.assert_allclose(o[0, 0, 2:, 0], exp_o, rtol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, 2:], exp_l, rtol=1e-12)
+
+
+# --------------------------------------------------------- independent library
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal", [
+    (1, 4, 2, 37, 16, True), (2, 6, 3, 50, 8, False), (1, 8, 1, 33, 32, True),
+    (2, 4, 4, 19, 64, True), (1, 4, 2, 128, 64, True),
+])
+def test_matches_torch_sdpa_fp64(B, Hq, Hkv, S, D, causal):
+    """torch's own CPU scaled_dot_product_attention in float64 (its math
+    path; GQA via enable_gqa, which repeats each K/V head for consecutive
+    query heads) is an independent implementation of the same definition."""
+    q = _rand((B, Hq, S, D), 1)
+    k = _rand((B, Hkv, S, D), 2)
+    v = _rand((B, Hkv, S, D), 3)
+    scale = 1.0 / math.sqrt(D) * 1.7
+    o, _ = ref_prefill(q, k, v, causal=causal, scale=scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        is_causal=causal, scale=scale, enable_gqa=True).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ closed forms
+
+def test_causal_row0_is_v0_and_lse_is_score():
+    B, Hq, Hkv, S, D = 2, 4, 2, 24, 16
+    q, k, v = _rand((B, Hq, S, D), 4), _rand((B, Hkv, S, D), 5), _rand((B, Hkv, S, D), 6)
+    scale = 0.3
+    o, lse = ref_prefill(q, k, v, causal=True, scale=scale)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            np.testing.assert_allclose(o[b, h, 0], v[b, g, 0], atol=1e-14)
+            np.testing.assert_allclose(lse[b, h, 0], scale * q[b, h, 0] @ k[b, g, 0], atol=1e-13)
+
+
+def test_zero_query_gives_prefix_mean_and_log_count():
+    B, Hq, Hkv, S, D = 1, 2, 1, 20, 8
+    q = np.zeros((B, Hq, S, D))
+    k, v = _rand((B, Hkv, S, D), 7), _rand((B, Hkv, S, D), 8)
+    o, lse = ref_prefill(q, k, v, causal=True, scale=1.0)
+    for i in range(S):
+        np.testing.assert_allclose(o[0, 1, i], v[0, 0, : i + 1].mean(axis=0), atol=1e-14)
+        np.testing.assert_allclose(lse[0, 1, i], math.log(i + 1), atol=1e-14)
+    o, lse = ref_prefill(q, k, v, causal=False, scale=1.0)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0].mean(axis=0), (S, D)), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], math.log(S), atol=1e-14)
+
+
+def test_constant_v_gives_constant_output():
+    q, k = _rand((1, 4, 30, 16), 9), _rand((1, 2, 30, 16), 10)
+    v = np.full((1, 2, 30, 16), -2.75)
+    o, _ = ref_prefill(q, k, v, causal=True, scale=0.25)
+    np.testing.assert_allclose(o, -2.75, atol=1e-14)
+
+
+def test_dominant_key_selects_its_value():
+    S, D = 12, 4
+    q = np.zeros((1, 1, S, D)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, S, D)); k[0, 0, 5, 0] = 80.0     # gap of 80 nats
+    v = _rand((1, 1, S, D), 11)
+    o, lse = ref_prefill(q, k, v, causal=True, scale=1.0)
+    np.testing.assert_allclose(o[0, 0, 5:], np.broadcast_to(v[0, 0, 5], (S - 5, D)), atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0, 5:], 80.0, atol=1e-12)
+
+
+# ------------------------------------------------------------------- invariants
+
+def test_identity_values_expose_probabilities():
+    """With V = I (D = S) the output rows are the probability rows: they are
+    non-negative, sum to 1 and vanish above the diagonal when causal."""
+    S = 16
+    q, k = _rand((1, 2, S, S), 12), _rand((1, 1, S, S), 13)
+    v = np.eye(S)[None, None]
+    p, _ = ref_prefill(q, k, v, causal=True, scale=0.5)
+    assert (p >= 0).all()
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-14)
+    assert np.all(np.triu(p[0, 0], 1) == 0) and np.all(np.triu(p[0, 1], 1) == 0)
+
+
+def test_gqa_equals_mha_on_repeated_kv_and_mqa():
+    B, Hq, S, D = 2, 8, 21, 16
+    q = _rand((B, Hq, S, D), 14)
+    for Hkv in (1, 2, 4, 8):
+        k, v = _rand((B, Hkv, S, D), 15 + Hkv), _rand((B, Hkv, S, D), 25 + Hkv)
+        o, l = ref_prefill(q, k, v, causal=True, scale=0.2)
+        kr = np.repeat(k, Hq // Hkv, axis=1)
+        vr = np.repeat(v, Hq // Hkv, axis=1)
+        o2, l2 = ref_prefill(q, kr, vr, causal=True, scale=0.2)
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(l, l2)
+    assert [kv_head_of(h, 32, 8) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+
+
+def test_noncausal_key_permutation_invariance():
+    q, k, v = _rand((1, 2, 25, 8), 30), _rand((1, 2, 25, 8), 31), _rand((1, 2, 25, 8), 32)
+    perm = np.random.default_rng(33).permutation(25)
+    o, l = ref_prefill(q, k, v, causal=False, scale=0.7)
+    o2, l2 = ref_prefill(q, k[:, :, perm], v[:, :, perm], causal=False, scale=0.7)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(l, l2, atol=1e-13)
+
+
+def test_lse_merge_over_key_partition():
+    """The log-sum-exp of the whole row equals ln(sum_s exp(lse_s)) over any
+    partition of the keys into parts, and O is the exp(lse_s - lse)-weighted
+    sum of the parts' outputs (the identity split-KV decoding relies on)."""
+    rng = np.random.default_rng(40)
+    L, D, Hq, Hkv = 57, 16, 4, 2
+    q = rng.standard_normal((1, Hq, L, D)); k = rng.standard_normal((1, Hkv, L, D))
+    v = rng.standard_normal((1, Hkv, L, D))
+    o, lse = ref_prefill(q, k, v, causal=False, scale=0.4)
+    cuts = np.sort(rng.choice(np.arange(1, L), size=3, replace=False))
+    parts = np.split(np.arange(L), cuts)
+    os_, ls_ = [], []
+    for idx in parts:
+        # a part is attention restricted to its keys (non-causal)
+        op, lp = ref_prefill(q[:, :, : len(idx)] * 0 + q[:, :, :1], k[:, :, idx], v[:, :, idx],
+                             causal=False, scale=0.4)
+        os_.append(op[:, :, 0]); ls_.append(lp[:, :, 0])
+    ls_ = np.stack(ls_)                       # [parts, 1, Hq]
+    tot = np.log(np.sum(np.exp(ls_), axis=0))
+    np.testing.assert_allclose(tot, lse[:, :, 0], atol=1e-13)
+    w = np.exp(ls_ - tot)[..., None]
+    np.testing.assert_allclose(np.sum(w * np.stack(os_), axis=0), o[:, :, 0], atol=1e-13)
+
+
+# ----------------------------------------------------------------------- decode
+
+def _decode_small(tail="zero", seed=50, N=5):
+    return decode_inputs(N=N, Hq=8, Hkv=2, D=16, seed=seed, lmin=1, lmax=70, block_size=16,
+                         tail=tail, dtype="f32")
+
+
+def test_decode_equals_last_prefill_row():
+    d = _decode_small()
+    q, kp, vp = upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool)
+    o, lse = ref_decode_paged(q, kp, vp, d.block_table.numpy(), d.seq_lens.numpy(),
+                              d.block_size, d.scale)
+    for n in range(d.N):
+        L = int(d.seq_lens[n])
+        t = np.arange(L)
+        phys = d.block_table.numpy()[n, t // 16]
+        kl = kp[phys, :, t % 16, :].transpose(1, 0, 2)[None]     # [1,Hkv,L,D]
+        vl = vp[phys, :, t % 16, :].transpose(1, 0, 2)[None]
+        qq = np.zeros((1, d.Hq, L, d.D)); qq[0, :, L - 1] = q[n]
+        op, lp = ref_prefill(qq, kl, vl, causal=True, scale=d.scale, rows=[L - 1])
+        np.testing.assert_allclose(o[n], op[0, :, 0], atol=1e-13)
+        np.testing.assert_allclose(lse[n], lp[0, :, 0], atol=1e-13)
+
+
+def test_decode_invariant_under_physical_permutation_and_nan_tails():
+    d = _decode_small(tail="nan")
+    q, kp, vp = upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool)
+    bt = d.block_table.numpy()
+    o, lse = ref_decode_paged(q, kp, vp, bt, d.seq_lens.numpy(), 16, d.scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    perm = np.random.default_rng(51).permutation(kp.shape[0])   # old -> new position
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1)
+    o2, lse2 = ref_decode_paged(q, kp2, vp2, bt2, d.seq_lens.numpy(), 16, d.scale)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_decode_empty_sequence():
+    d = decode_inputs(N=3, Hq=4, Hkv=2, D=8, seed=52, lens=[0, 5, 17], dtype="f32")
+    o, lse = ref_decode_paged(upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool),
+                              d.block_table.numpy(), d.seq_lens.numpy(), 16, d.scale)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.isfinite(o[1:]).all()
+
+
+# -------------------------------------------------------------------- blockskip
+
+def _sequential_blockskip(q, k, v, scale, lam, T):
+    """The online algorithm replayed tile by tile for one head: a running
+    max m and sum l per row, key tiles in ascending order, each tile's row
+    maxima tested against m BEFORE the tile is folded in; skipped tiles are
+    not folded in at all.  Independent of the prefix-max formulation."""
+    S, D = q.shape
+    ln_lam = math.log(lam)
+    nT = (S + T - 1) // T
+    O = np.zeros((S, D)); LSE = np.zeros(S)
+    skip = np.zeros((nT, nT), dtype=bool)
+    for qt in range(nT):
+        rows = np.arange(qt * T, min(S, (qt + 1) * T))
+        m = np.full(len(rows), -np.inf); l = np.zeros(len(rows)); acc = np.zeros((len(rows), D))
+        for kt in range(qt + 1):
+            cols = np.arange(kt * T, min(S, (kt + 1) * T))
+            s = scale * q[rows] @ k[cols].T
+            s[cols[None, :] > rows[:, None]] = -np.inf
+            tm = s.max(axis=1)
+            with np.errstate(invalid="ignore"):
+                neg = np.isneginf(tm) | (np.isfinite(m) & (tm - m < ln_lam))
+            if neg.all():
+                skip[qt, kt] = True
+                continue
+            m_new = np.maximum(m, tm)
+            alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m_new))
+            p = np.exp(s - m_new[:, None])
+            l = alpha * l + p.sum(axis=1)
+            acc = alpha[:, None] * acc + p @ v[cols]
+            m = m_new
+        O[rows] = acc / l[:, None]
+        LSE[rows] = m + np.log(l)
+    return O, LSE, skip
+
+
+@pytest.mark.parametrize("S,amp,lam", [(96, 12.0, 1e-3), (128, 12.0, 1e-2), (80, 3.0, 1e-3),
+                                       (150, 20.0, 0.3)])
+def test_blockskip_prefix_max_equals_sequential_replay(S, amp, lam):
+    from workloads import blockskip_inputs
+    T = 16
+    w = blockskip_inputs(1, 2, 1, S, 16, seed=60, amplitude=amp, n_sinks=4,
+                         boosted="second_half", dtype="f32", scale=0.25)
+    q, k, v = upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v)
+    o, lse, skip, _ = ref_blockskip(q, k, v, scale=w.scale, lam=lam, tile=T)
+    for h in range(2):
+        so, sl, ss = _sequential_blockskip(q[0, h], k[0, 0], v[0, 0], w.scale, lam, T)
+        np.testing.assert_array_equal(skip[0, h], ss)
+        np.testing.assert_allclose(o[0, h], so, atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], sl, atol=1e-12)
+    if amp >= 12:
+        assert skip.any(), "stress inputs must exercise the skip path"
+
+
+def test_blockskip_tiny_lambda_is_exact_attention_and_error_bound():
+    from workloads import blockskip_inputs
+    w = blockskip_inputs(1, 2, 1, 128, 16, seed=61, amplitude=12.0, n_sinks=4,
+                         boosted="second_half", dtype="f32", scale=0.25)
+    q, k, v = upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v)
+    o_ex, l_ex = ref_prefill(q, k, v, causal=True, scale=w.scale)
+    o0, l0, s0, _ = ref_blockskip(q, k, v, scale=w.scale, lam=1e-300, tile=16)
+    assert not s0.any()
+    np.testing.assert_allclose(o0, o_ex, atol=1e-13)
+    np.testing.assert_allclose(l0, l_ex, atol=1e-13)
+    o1, l1, s1, _ = ref_blockskip(q, k, v, scale=w.scale, lam=1e-3, tile=16)
+    assert s1.any()
+    # dropped probability mass per row: 1 - exp(LSE_kept - LSE_full); the
+    # output moves by at most 2 * max|V| times that mass
+    mass = 1.0 - np.exp(l1 - l_ex)
+    err = np.abs(o1 - o_ex).max(axis=-1)
+    assert np.all(err <= 2 * np.abs(v).max() * mass + 1e-12)
+    assert np.all(l1 <= l_ex + 1e-13)
+
+
+def test_blockskip_qtile_subset_matches_full():
+    from workloads import blockskip_inputs
+    w = blockskip_inputs(1, 4, 2, 96, 8, seed=62, amplitude=12.0, n_sinks=3,
+                         boosted="second_half", dtype="f32", scale=0.35)
+    q, k, v = upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v)
+    o, l, s, g = ref_blockskip(q, k, v, scale=w.scale, lam=1e-3, tile=16)
+    sel = [1, 4, 5]
+    o2, l2, s2, g2 = ref_blockskip(q, k, v, scale=w.scale, lam=1e-3, tile=16, qtiles=sel)
+    rows = np.concatenate([np.arange(t * 16, (t + 1) * 16) for t in sel])
+    np.testing.assert_array_equal(o[:, :, rows], o2)
+    np.testing.assert_array_equal(s[:, :, sel], s2)

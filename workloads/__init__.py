@@ -1,0 +1,233 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and lays them out in memory.  It holds
+none of the attention arithmetic, so both the fp64 oracle and the HIP library
+can be fed from it without sharing any of the method's code.
+
+Every tensor is produced on the host (CPU).  Floating-point samples are drawn
+as float32 from numpy's PCG64 generator and then rounded to the working dtype
+with a round-to-nearest-even cast (torch's ``Tensor.to(torch.bfloat16)``).
+Consumers must treat the rounded tensor as THE input: the oracle upcasts it
+exactly to fp64, the GPU reads it as is.
+
+Shapes follow the prefill problem statement on the FlashAttention/TensorRT-LLM
+page ("flash-attention与TensorRT-LLM集成", section on how FlashAttention
+works: Q, K, V are split into blocks), with the grouped-query head layout of
+the TensorRT GQA page ("TensorRT对Grouped Query Attention的支持进展",
+technical background: query heads split into groups that share one K/V head)
+and the paged KV cache of the PagedAttention description ("TensorRT-LLM：大模型
+推理加速的工业级引擎", PagedAttention section: fixed-size blocks plus a block
+table mapping logical to physical blocks).
+
+Layouts:
+  * prefill Q/O: [B, Hq, S, D]; K/V: [B, Hkv, S, D] (contiguous, row-major)
+  * decode q/o: [N, Hq, D]; k_pool/v_pool: [NB, Hkv, block_size, D];
+    block_table: int32 [N, max_blocks_per_seq] (padding -1); seq_lens: int32 [N]
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "PrefillInputs", "DecodeInputs", "CONFIGS",
+    "prefill_inputs", "blockskip_inputs", "decode_inputs", "to_dtype",
+    "upcast_f64", "prefill_flops",
+]
+
+
+def to_dtype(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """Round a float32 numpy array to ``dtype`` ("bf16" or "f32") on the CPU."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    if dtype == "f32":
+        return t.clone()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def upcast_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a CPU bf16/f32 tensor to a float64 numpy array."""
+    return t.to(torch.float64).numpy()
+
+
+def prefill_flops(B: int, Hq: int, S: int, D: int, causal: bool) -> int:
+    """Algorithmic flops of one prefill: 2*D per visible (query, key) pair for
+    Q.K^T and 2*D for P.V.  Causal visible pairs per head: S(S+1)/2."""
+    pairs = S * (S + 1) // 2 if causal else S * S
+    return 4 * B * Hq * D * pairs
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    causal: bool
+    scale: float
+    dtype: str
+    seed: int
+    # block-skip structure (None for plain prefill workloads)
+    sink_rows: Optional[np.ndarray] = None
+    boosted_rows: Optional[np.ndarray] = None
+    boost_dim: Optional[int] = None
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [N, Hq, D]
+    k_pool: torch.Tensor       # [NB, Hkv, block_size, D]
+    v_pool: torch.Tensor       # [NB, Hkv, block_size, D]
+    block_table: torch.Tensor  # int32 [N, max_blocks]
+    seq_lens: torch.Tensor     # int32 [N]
+    block_size: int
+    N: int
+    Hq: int
+    Hkv: int
+    D: int
+    max_blocks: int
+    scale: float
+    dtype: str
+    seed: int
+    perm: np.ndarray           # logical block id -> physical block id
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V the decode must read: sum_n L_n * Hkv * D * 2 tensors."""
+        esize = 2 if self.dtype == "bf16" else 4
+        return int(self.seq_lens.to(torch.int64).sum()) * self.Hkv * self.D * 2 * esize
+
+
+def prefill_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, *, seed: int,
+                   dtype: str = "bf16", causal: bool = True,
+                   scale: Optional[float] = None) -> PrefillInputs:
+    """i.i.d. N(0,1) Q, K, V drawn in that order as whole [B,H,S,D] tensors."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return PrefillInputs(to_dtype(q, dtype), to_dtype(k, dtype), to_dtype(v, dtype),
+                         B, Hq, Hkv, S, D, causal, float(scale), dtype, seed)
+
+
+def blockskip_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, *, seed: int,
+                     amplitude: float = 3.0, n_sinks: int = 64,
+                     boosted: str = "random_half", dtype: str = "bf16",
+                     scale: Optional[float] = None) -> PrefillInputs:
+    """Attention-sink structure for the block-skip workload.
+
+    Q, K, V are N(0,1) as in :func:`prefill_inputs`.  Then one coordinate
+    ``k`` in [0, D) is drawn (u = e_k), ``n_sinks`` key positions are drawn
+    without replacement (shared by every KV head and batch) and get
+    ``amplitude * e_k`` added, and half of the query positions get
+    ``amplitude * u`` added (shared by every query head and batch).
+    ``boosted`` is "random_half" (S/2 positions drawn without replacement) or
+    "second_half" (positions S/2 .. S-1, the stress variant).  The boost is
+    added to the float32 sample before rounding to ``dtype``.
+    """
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    kdim = int(rng.integers(0, D))
+    sinks = np.sort(rng.choice(S, size=min(n_sinks, S), replace=False))
+    if boosted == "random_half":
+        rows = np.sort(rng.choice(S, size=S // 2, replace=False))
+    elif boosted == "second_half":
+        rows = np.arange(S // 2, S)
+    else:
+        raise ValueError(boosted)
+    k[:, :, sinks, kdim] += np.float32(amplitude)
+    q[:, :, rows, kdim] += np.float32(amplitude)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return PrefillInputs(to_dtype(q, dtype), to_dtype(k, dtype), to_dtype(v, dtype),
+                         B, Hq, Hkv, S, D, True, float(scale), dtype, seed,
+                         sink_rows=sinks, boosted_rows=rows, boost_dim=kdim)
+
+
+def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
+                  lmin: int = 512, lmax: int = 4096, block_size: int = 16,
+                  tail: str = "zero", dtype: str = "bf16",
+                  lens: Optional[list] = None,
+                  scale: Optional[float] = None) -> DecodeInputs:
+    """Paged KV-cache decode inputs.
+
+    Draw order: the N context lengths (uniform integers on [lmin, lmax],
+    inclusive) unless ``lens`` is given, then q [N,Hq,D], then for each
+    sequence its logical K and V ([L,Hkv,D] each, K first), then one random
+    permutation of the NB = sum ceil(L/block_size) physical blocks.  Logical
+    block j of sequence n (numbered sequence-major, ``base_n + j``) lives in
+    physical block ``perm[base_n + j]``.  Unused slots of each sequence's last
+    block hold zeros (``tail="zero"``) or NaN (``tail="nan"``, which a correct
+    kernel never reads).  Padding entries of the block table are -1.
+    """
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens_np = rng.integers(lmin, lmax, size=N, endpoint=True).astype(np.int64)
+    else:
+        lens_np = np.asarray(lens, dtype=np.int64)
+        assert lens_np.shape == (N,)
+    q = rng.standard_normal((N, Hq, D), dtype=np.float32)
+    nblk = [(int(L) + block_size - 1) // block_size for L in lens_np]
+    NB = int(sum(nblk))
+    max_blocks = max(1, max(nblk) if nblk else 1)
+    fill = np.nan if tail == "nan" else 0.0
+    kp = np.full((NB, Hkv, block_size, D), fill, dtype=np.float32)
+    vp = np.full((NB, Hkv, block_size, D), fill, dtype=np.float32)
+    logical_k, logical_v = [], []
+    for n in range(N):
+        L = int(lens_np[n])
+        logical_k.append(rng.standard_normal((L, Hkv, D), dtype=np.float32))
+        logical_v.append(rng.standard_normal((L, Hkv, D), dtype=np.float32))
+    perm = rng.permutation(NB) if NB > 0 else np.zeros(0, dtype=np.int64)
+    table = np.full((N, max_blocks), -1, dtype=np.int32)
+    base = 0
+    for n in range(N):
+        L = int(lens_np[n])
+        for j in range(nblk[n]):
+            p = int(perm[base + j])
+            table[n, j] = p
+            t0, t1 = j * block_size, min(L, (j + 1) * block_size)
+            # [tokens, Hkv, D] -> [Hkv, tokens, D]
+            kp[p, :, : t1 - t0, :] = logical_k[n][t0:t1].transpose(1, 0, 2)
+            vp[p, :, : t1 - t0, :] = logical_v[n][t0:t1].transpose(1, 0, 2)
+        base += nblk[n]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return DecodeInputs(
+        q=to_dtype(q, dtype), k_pool=to_dtype(kp, dtype), v_pool=to_dtype(vp, dtype),
+        block_table=torch.from_numpy(table), seq_lens=torch.from_numpy(lens_np.astype(np.int32)),
+        block_size=block_size, N=N, Hq=Hq, Hkv=Hkv, D=D, max_blocks=max_blocks,
+        scale=float(scale), dtype=dtype, seed=seed, perm=perm)
+
+
+# The five named workloads.  Sizes are the problem statement's; seeds are fixed
+# so that every consumer (tests, bench, oracle timing) sees the same tensors.
+CONFIGS = {
+    "tiny_gqa_f32": dict(kind="prefill", B=1, Hq=4, Hkv=2, S=128, D=64, dtype="f32",
+                         causal=True, seed=1001),
+    "mha_causal_s2048": dict(kind="prefill", B=4, Hq=32, Hkv=32, S=2048, D=128, dtype="bf16",
+                             causal=True, seed=1002),
+    "gqa_causal_s8192": dict(kind="prefill", B=1, Hq=32, Hkv=8, S=8192, D=128, dtype="bf16",
+                             causal=True, seed=1003),
+    "paged_decode_gqa": dict(kind="decode", N=64, Hq=32, Hkv=8, D=128, lmin=512, lmax=4096,
+                             block_size=16, dtype="bf16", seed=1004),
+    "blockskip_s32768": dict(kind="blockskip", B=1, Hq=32, Hkv=8, S=32768, D=128, dtype="bf16",
+                             amplitude=3.0, boosted="random_half", seed=1005,
+                             lam=1e-3, tile=64),
+}
