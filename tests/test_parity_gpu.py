@@ -1,0 +1,253 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Tolerances (max-abs, on O and on LSE): 2e-2 for bf16 inputs with fp32
+accumulation, 1e-4 for float32 inputs.  Block-skip decisions must equal the
+oracle's on every tile whose decision margin |gap - ln(lambda)| is at least
+1e-3 (the oracle's gap is fp64, the kernel's fp32; tiles inside that margin
+are reported, and none occur in the seeded workloads below).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_flash_attn_fwd_amd as A
+from oracle import ref_blockskip, ref_decode_paged, ref_prefill
+from workloads import CONFIGS, blockskip_inputs, decode_inputs, prefill_inputs, upcast_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run_prefill(w):
+    dev = "cuda"
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    o, lse = A.prefill(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _compare(o, lse, ro, rl, tol, what):
+    eo = float(np.max(np.abs(o.astype(np.float64) - ro)))
+    el = float(np.max(np.abs(lse.astype(np.float64) - rl)))
+    say(f"{what}: max|dO|={eo:.3e} max|dLSE|={el:.3e} (tol {tol})")
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert eo <= tol, f"{what}: O error {eo}"
+    assert el <= tol, f"{what}: LSE error {el}"
+
+
+# ------------------------------------------------------------------- prefill
+
+def test_tiny_gqa_f32_full():
+    c = CONFIGS["tiny_gqa_f32"]
+    say("tiny_gqa_f32 B1 Hq4 Hkv2 S128 D64 fp32")
+    w = prefill_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"], dtype="f32")
+    o, lse = _run_prefill(w)
+    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=True,
+                         scale=w.scale)
+    _compare(o, lse, ro, rl, TOL["f32"], "tiny_gqa_f32")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal", [
+    (1, 4, 2, 200, 128, True),     # GQA, ragged tail, several tiles
+    (2, 4, 4, 333, 64, True),      # MHA, D=64
+    (1, 8, 2, 257, 128, False),    # non-causal GQA
+    (1, 8, 1, 130, 128, True),     # MQA
+    (1, 16, 2, 300, 128, True),    # group of 8 heads
+    (1, 6, 2, 190, 64, True),      # group of 3 heads
+    (1, 2, 2, 1, 128, True),       # single token
+    (1, 4, 1, 63, 64, False),      # one partial tile
+    (1, 4, 4, 513, 128, True),     # MHA, 256-row workgroups + tail
+])
+def test_prefill_bf16_small(B, Hq, Hkv, S, D, causal):
+    say(f"prefill bf16 B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} causal={causal}")
+    w = prefill_inputs(B, Hq, Hkv, S, D, seed=11 + S, causal=causal)
+    o, lse = _run_prefill(w)
+    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=causal,
+                         scale=w.scale)
+    _compare(o, lse, ro, rl, TOL["bf16"], "small")
+
+
+def test_prefill_f32_variants():
+    for (B, Hq, Hkv, S, D, causal) in [(1, 4, 2, 77, 128, True), (2, 2, 1, 50, 64, False)]:
+        say(f"prefill f32 B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} causal={causal}")
+        w = prefill_inputs(B, Hq, Hkv, S, D, seed=5 + S, causal=causal, dtype="f32")
+        o, lse = _run_prefill(w)
+        ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=causal,
+                             scale=w.scale)
+        _compare(o, lse, ro, rl, TOL["f32"], "f32")
+
+
+def _sampled_rows(S, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(S, size=n, replace=False).tolist())
+    rows |= {0, 1, 63, 64, S // 2, S - 2, S - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["mha_causal_s2048", "gqa_causal_s8192"])
+def test_prefill_full_size_sampled_rows(name):
+    c = CONFIGS[name]
+    say(f"{name} full size, sampled rows")
+    w = prefill_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"])
+    o, lse = _run_prefill(w)
+    rows = _sampled_rows(c["S"], 48, 7)
+    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=True,
+                         scale=w.scale, rows=rows)
+    _compare(o[:, :, rows], lse[:, :, rows], ro, rl, TOL["bf16"], name)
+    # property at every row: |O| is bounded by max |V| of the visible prefix
+    assert np.abs(o).max() <= float(w.v.float().abs().max()) + 1e-2
+
+
+# -------------------------------------------------------------------- decode
+
+def _run_decode(d, table=None, lens=None, k_pool=None, v_pool=None):
+    dev = "cuda"
+    q = d.q.to(dev)
+    kp = (d.k_pool if k_pool is None else k_pool).to(dev)
+    vp = (d.v_pool if v_pool is None else v_pool).to(dev)
+    bt = (d.block_table if table is None else table).to(dev)
+    sl = (d.seq_lens if lens is None else lens).to(dev)
+    o, lse = A.decode_paged(q, kp, vp, bt, sl, d.block_size, d.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _ref_decode(d, table=None, lens=None):
+    bt = (d.block_table if table is None else table).numpy()
+    sl = (d.seq_lens if lens is None else lens).numpy()
+    return ref_decode_paged(upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool), bt, sl,
+                            d.block_size, d.scale)
+
+
+def test_paged_decode_full_config_nan_tails():
+    c = CONFIGS["paged_decode_gqa"]
+    say("paged_decode_gqa full config, NaN-poisoned tail slots")
+    d = decode_inputs(c["N"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], lmin=c["lmin"],
+                      lmax=c["lmax"], tail="nan")
+    o, lse = _run_decode(d)
+    ro, rl = _ref_decode(d)
+    _compare(o, lse, ro, rl, TOL["bf16"], "decode c4")
+
+
+def test_paged_decode_permutation_bit_identical():
+    say("decode: physical block permutation leaves the output bit-identical")
+    d = decode_inputs(8, 32, 8, 128, seed=77, lmin=1, lmax=700)
+    o1, l1 = _run_decode(d)
+    perm = torch.from_numpy(np.random.default_rng(78).permutation(d.num_blocks))
+    kp2 = torch.empty_like(d.k_pool); kp2[perm] = d.k_pool
+    vp2 = torch.empty_like(d.v_pool); vp2[perm] = d.v_pool
+    bt = d.block_table.clone()
+    m = bt >= 0
+    bt[m] = perm[bt[m].long()].to(torch.int32)
+    o2, l2 = _run_decode(d, table=bt, k_pool=kp2, v_pool=vp2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ro, rl = _ref_decode(d)
+    _compare(o1, l1, ro, rl, TOL["bf16"], "decode perm")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 128), (16, 1, 64), (8, 4, 64),
+                                       (32, 2, 128)])
+def test_paged_decode_edge_lengths(Hq, Hkv, D):
+    lens = [1, 15, 16, 17, 255, 256, 257, 1000, 0, 513]
+    say(f"decode edge lengths Hq{Hq} Hkv{Hkv} D{D} lens={lens}")
+    d = decode_inputs(len(lens), Hq, Hkv, D, seed=90 + D, lens=lens, tail="nan")
+    o, lse = _run_decode(d)
+    ro, rl = _ref_decode(d)
+    assert np.all(o[8] == 0) and np.all(np.isneginf(lse[8]))
+    keep = [i for i in range(len(lens)) if lens[i] > 0]
+    _compare(o[keep], lse[keep], ro[keep], rl[keep], TOL["bf16"], "decode edges")
+
+
+def test_paged_decode_bad_table_entries_give_nan():
+    say("decode: out-of-range table entry and too-long sequence -> NaN rows only")
+    d = decode_inputs(4, 8, 2, 128, seed=95, lens=[40, 40, 40, 40])
+    bt = d.block_table.clone()
+    bt[1, 2] = d.num_blocks + 5          # out of range, inside the used blocks
+    bt[2, 0] = -7
+    lens = d.seq_lens.clone()
+    lens[3] = d.max_blocks * 16 + 1      # longer than the table row
+    o, lse = _run_decode(d, table=bt, lens=lens)
+    assert np.isnan(o[1]).all() and np.isnan(lse[1]).all()
+    assert np.isnan(o[2]).all() and np.isnan(o[3]).all()
+    ro, rl = _ref_decode(d)
+    _compare(o[:1], lse[:1], ro[:1], rl[:1], TOL["bf16"], "decode good row")
+
+
+# ---------------------------------------------------------------- block skip
+
+def _run_blockskip(w, lam):
+    q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
+    o, lse, bm, cnt = A.prefill_blockskip(q, k, v, scale=w.scale, lam=lam)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), bm.cpu().numpy(), int(cnt.item())
+
+
+def _check_decisions(bm, skip, gap, lam, qtiles, what):
+    ln_lam = math.log(lam)
+    nT = bm.shape[-1]
+    live = np.zeros_like(skip)
+    for i, qt in enumerate(qtiles):
+        live[:, :, i, : qt + 1] = True
+    gpu = bm[:, :, qtiles, :].astype(bool) & live
+    border = live & (np.abs(gap - ln_lam) < 1e-3)
+    mism = (gpu != skip) & live & ~border
+    say(f"{what}: skipped {int(skip.sum())}/{int(live.sum())} live tiles, "
+        f"borderline {int(border.sum())}, mismatches {int(mism.sum())}")
+    assert mism.sum() == 0
+    return int(border.sum())
+
+
+def test_blockskip_stress_full_decisions():
+    say("block skip stress: S=4096 amplitude 12, second half boosted")
+    w = blockskip_inputs(1, 8, 2, 4096, 128, seed=1105, amplitude=12.0, boosted="second_half")
+    o, lse, bm, cnt = _run_blockskip(w, 1e-3)
+    q, k, v = upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v)
+    ro, rl, skip, gap = ref_blockskip(q, k, v, scale=w.scale, lam=1e-3, tile=64)
+    nT = 4096 // 64
+    _check_decisions(bm, skip, gap, 1e-3, np.arange(nT), "stress")
+    live = 8 * nT * (nT + 1) // 2
+    assert skip.sum() > 0.1 * live, "stress inputs must exercise the skip path"
+    assert cnt == int(bm.astype(np.int64).sum())
+    _compare(o, lse, ro, rl, TOL["bf16"], "stress O/LSE")
+
+
+def test_blockskip_small_lambda_equals_dense():
+    say("block skip with lambda=1e-30 equals the dense kernel")
+    w = blockskip_inputs(1, 4, 1, 700, 128, seed=1106, amplitude=12.0, boosted="second_half")
+    o, lse, bm, cnt = _run_blockskip(w, 1e-30)
+    assert cnt == 0 and bm.sum() == 0
+    od, ld = _run_prefill(w)
+    assert np.array_equal(o, od) and np.array_equal(lse, ld)
+
+
+def test_blockskip_full_config_sampled_qtiles():
+    c = CONFIGS["blockskip_s32768"]
+    say("blockskip_s32768 full size, sampled query tiles")
+    w = blockskip_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"],
+                         amplitude=c["amplitude"], boosted=c["boosted"])
+    o, lse, bm, cnt = _run_blockskip(w, c["lam"])
+    qt = np.array([0, 1, 7, 100, 256, 511])
+    heads = [0, 13, 31]
+    res = []
+    for h in heads:
+        g = h // (c["Hq"] // c["Hkv"])
+        res.append(ref_blockskip(upcast_f64(w.q[:, h:h + 1]), upcast_f64(w.k[:, g:g + 1]),
+                                 upcast_f64(w.v[:, g:g + 1]), scale=w.scale, lam=c["lam"],
+                                 tile=64, qtiles=qt))
+    ro, rl, skip, gap = (np.concatenate([r[i] for r in res], axis=1) for i in range(4))
+    _check_decisions(bm[:, heads], skip, gap, c["lam"], qt, "c5 sampled")
+    rows = np.concatenate([np.arange(t * 64, (t + 1) * 64) for t in qt])
+    _compare(o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl, TOL["bf16"], "c5 O/LSE")
+    nT = c["S"] // 64
+    live = c["B"] * c["Hq"] * nT * (nT + 1) // 2
+    say(f"c5 skipped fraction {cnt / live:.6f} ({cnt}/{live})")
