@@ -71,24 +71,78 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Value of x in the lane 32 positions away (v_permlane32_swap exchanges the
+// two halves of the wave); fn must be symmetric, e.g. max or add.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes at gbase + voff land at LDS byte lds_addr + 16*i.  The
+// instruction is issued from asm so that the compiler does not serialise it
+// against unrelated LDS reads; its completion is awaited explicitly with
+// wait_vmem before the workgroup barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(gbase), "s"(m) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS layout of one pipeline stage: a K tile then a V tile, BN rows each,
+// row-major with padded rows.  K rows are D*2+16 bytes: the 16-byte K
+// fragment reads of 16 consecutive rows then fall in distinct banks.  V rows
+// are D*2+64 bytes: the transposing 8-byte reads of 4 rows x 64 bytes per
+// half-wave fall in distinct banks.  Both paddings keep every fragment
+// address a lane base plus a compile-time offset.  Tiles are filled with
+// 1 KiB DMA blocks that also cover the pad slots (loaded with a dummy,
+// in-bounds chunk).
 template <int D>
 struct Tile {
-  static constexpr int KSTR = D + 8;    // bf16 per K row in LDS (16-byte pad)
-  static constexpr int VSTR = BN + 8;   // bf16 per V^T row in LDS (16-byte pad)
-  static constexpr int KT = BN * KSTR;  // elements of one K tile
-  static constexpr int VT = D * VSTR;   // elements of one V^T tile
-  static constexpr int CH = D / 8;      // 16-byte chunks per row
-  static constexpr int KITEMS = BN * CH / kThreads;
-  static constexpr int VITEMS = (BN / 2) * CH;  // (key pair, chunk) items
-  static constexpr size_t lds_bytes = 2 * (size_t)(KT + VT) * 2;
+  static constexpr int CH = D / 8;            // 16-byte chunks of one row
+  static constexpr int KSL = CH + 1;          // K row: slots of 16 bytes
+  static constexpr int VSL = CH + 4;          // V row
+  static constexpr int RB = D * 2;            // bytes of one global row
+  static constexpr int RK = KSL * 16, RV = VSL * 16;
+  static constexpr int KT = BN * RK;          // = KSL KiB
+  static constexpr int VT = BN * RV;          // = VSL KiB
+  static constexpr int STAGE = KT + VT;
+  static constexpr int NST = 3;               // pipeline depth (tiles in flight)
+  static constexpr size_t lds_bytes = (size_t)NST * STAGE;
+  // DMA blocks issued by wave w per tile: blocks w, w+8, ... of KSL + VSL
+  static __device__ __forceinline__ int dma_count(int w) {
+    return (KSL - w + kWaves - 1) / kWaves + (VSL - w + kWaves - 1) / kWaves;
+  }
 };
+
+#define LDS_AS __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D, bool CAUSAL, bool SKIP>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   using T = Tile<D>;
   constexpr int NKS = D / 16;  // 16-dim k-steps of Q.K^T
   constexpr int NDB = D / 32;  // 32-dim output blocks of P.V
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   __shared__ int skip_flag[2][kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -111,6 +165,42 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   const bool has_rows = q0 < S;
   const int wave_tiles = !has_rows ? 0 : (CAUSAL ? min(S - 1, q0 + 31) / BN + 1 : n_tiles);
 
+  const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
+  const uint16_t* Kg = p.k + kvbase;
+  const uint16_t* Vg = p.v + kvbase;
+
+  // ---- asynchronous global -> LDS copy of tile t into stage t % NST.
+  // One wave-wide load fills 1 KiB of LDS (16 bytes per lane, in lane
+  // order); the lane fetches the global chunk that the swizzle puts there.
+  // Keys past the end are clamped to the last key and masked later.
+  auto issue = [&](int t) {
+    const uint32_t st = smem_base + (t % T::NST) * T::STAGE;
+    const int key0 = t * BN;
+#pragma unroll
+    for (int i = wave; i < T::KSL; i += kWaves) {
+      const int g = i * 64 + lane, r = g / T::KSL, c = g % T::KSL;
+      const uint32_t off = (uint32_t)min(key0 + r, S - 1) * T::RB + (c < T::CH ? c : 0) * 16;
+      dma16(Kg, off, st + i * 1024);
+    }
+#pragma unroll
+    for (int i = wave; i < T::VSL; i += kWaves) {
+      const int g = i * 64 + lane, r = g / T::VSL, c = g % T::VSL;
+      const uint32_t off = (uint32_t)min(key0 + r, S - 1) * T::RB + (c < T::CH ? c : 0) * 16;
+      dma16(Vg, off, st + T::KT + i * 1024);
+    }
+  };
+  const int n_dma = T::dma_count(wave);
+  // wait until only the DMA blocks of the newest tile are in flight
+  auto wait_all_but_newest = [&]() {
+    switch (n_dma) {
+      case 2: wait_vmem<2>(); break;
+      case 3: wait_vmem<3>(); break;
+      case 4: wait_vmem<4>(); break;
+      case 5: wait_vmem<5>(); break;
+      default: wait_vmem<6>(); break;
+    }
+  };
+
   // ---- Q fragment (B operand): query q0+n, dims ks*16 + hf*8 .. +7
   const size_t qbase = ((size_t)b * p.Hq + head) * S;
   bf16x8 qf[NKS];
@@ -120,96 +210,70 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
+  // Complete the Q loads with a wait the compiler can see (vmcnt(0)), so it
+  // places no vector-memory waits of its own inside the loop, where they
+  // would also drain the tile prefetches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  issue(0);
+  if (n_tiles > 1) issue(1);
 
-  const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
-  const uint16_t* Kg = p.k + kvbase;
-  const uint16_t* Vg = p.v + kvbase;
-
-  // ---- global -> register staging of one K/V tile
-  u32x4 kreg[T::KITEMS];
-  u32x4 vreg0, vreg1;
-  auto load_tile = [&](int t) {
-    const int c0 = t * BN;
-#pragma unroll
-    for (int i = 0; i < T::KITEMS; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / T::CH, c = idx % T::CH;
-      const int key = c0 + r;
-      kreg[i] = key < S ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8)
-                        : u32x4{0, 0, 0, 0};
-    }
-    if (tid < T::VITEMS) {
-      const int tp = tid / T::CH, c = tid % T::CH;
-      const int key = c0 + 2 * tp;
-      vreg0 = key < S ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + c * 8)
-                      : u32x4{0, 0, 0, 0};
-      vreg1 = key + 1 < S ? *reinterpret_cast<const u32x4*>(Vg + (size_t)(key + 1) * D + c * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
-  };
-  // ---- register -> LDS: K row-major, V transposed and key-permuted
-  auto store_tile = [&](uint16_t* kl, uint16_t* vl) {
-#pragma unroll
-    for (int i = 0; i < T::KITEMS; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / T::CH, c = idx % T::CH;
-      *reinterpret_cast<u32x4*>(kl + r * T::KSTR + c * 8) = kreg[i];
-    }
-    if (tid < T::VITEMS) {
-      const int tp = tid / T::CH, c = tid % T::CH;
-      // key pair (2tp, 2tp+1) lies in one 4-key chunk; within each 16-key
-      // group the chunk order 0,1,2,3 is stored as 0,2,1,3
-      const int key = 2 * tp;
-      const int q4 = (key >> 2) & 3;
-      const int posq = q4 == 1 ? 2 : (q4 == 2 ? 1 : q4);
-      const int pos = (key & ~15) | (posq << 2) | (key & 3);
-      const int grp = (pos >> 3) ^ (c & 7);  // 8-key group, XOR-swizzled by dim/8
-      const int col = (grp << 3) | (pos & 7);
-      uint16_t* dst = vl + (c * 8) * T::VSTR + col;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = vreg0[j], bb = vreg1[j];
-        const uint32_t even = (a & 0xffffu) | (bb << 16);          // dim c*8 + 2j
-        const uint32_t odd = (a >> 16) | (bb & 0xffff0000u);       // dim c*8 + 2j + 1
-        *reinterpret_cast<uint32_t*>(dst + (2 * j) * T::VSTR) = even;
-        *reinterpret_cast<uint32_t*>(dst + (2 * j + 1) * T::VSTR) = odd;
-      }
-    }
-  };
+  // per-lane LDS offsets of the MFMA operand reads (see Tile)
+  const int k_base = n * T::RK + hf * 16;                 // + kb*32*RK + ks*32
+  const int vg = lane >> 4, vs = lane & 15;
+  const int v_base = ((vg >> 1) * 4 + (vs >> 2)) * T::RV + ((vg & 1) * 16 + 4 * (vs & 3)) * 2;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  float m = kUnset, l = 0.f;
+  float m_used = kUnset;   // reference max of the exponentials (log2 units)
+  float m_true = kUnset;   // running max (block skip decisions)
+  float l = 0.f;
+  unsigned skipped = 0;
   const float sl2 = p.sl2;
 
-  load_tile(0);
-  store_tile(smem, smem + T::KT);
-  __syncthreads();
-
+  int stage_off = 0;  // LDS offset of stage t % NST
   for (int t = 0; t < n_tiles; ++t) {
-    const uint16_t* kl = smem + (t & 1) * (T::KT + T::VT);
-    const uint16_t* vl = kl + T::KT;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
+    block_barrier();
+    if (t + 2 < n_tiles) issue(t + 2);
+    const LDS_AS unsigned char* kl = smem + stage_off;
+    stage_off = stage_off == (T::NST - 1) * T::STAGE ? 0 : stage_off + T::STAGE;
+    const LDS_AS unsigned char* vl = kl + T::KT;
     const bool active = t < wave_tiles;
     const int c0 = t * BN;
 
     f32x16 s[2];
     float tmx = -INFINITY;
     if (active) {
+      // two independent accumulator chains (key rows 0-31 and 32-63); the
+      // operand reads run one k-step ahead of the MFMAs
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
+      const LDS_AS unsigned char* kp = kl + k_base;
+      bf16x8 a0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp);
+      bf16x8 a1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(kl + (kb * 32 + n) * T::KSTR + ks * 16 + hf * 8);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 n0 = a0, n1 = a1;
+        if (ks + 1 < NKS) {
+          n0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + (ks + 1) * 32);
+          n1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK + (ks + 1) * 32);
         }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s[1], 0, 0, 0);
+        a0 = n0;
+        a1 = n1;
       }
+      // schedule: 4 operand reads ahead, then alternate MFMA / read
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NKS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       const bool need_mask = (c0 + BN > S) || (CAUSAL && c0 + BN - 1 > q0);
       if (need_mask) {
         const int qi = q0 + n;
@@ -221,13 +285,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
             if (key >= S || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
           }
       }
-      float mx = s[0][0];
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      tmx = mx * sl2;
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      tmx = half_swap_max(mx) * sl2;
     }
 
     bool skip_tile = false;
@@ -235,25 +298,36 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
       // BLASST test for this wave's 32 rows; the 64-row tile spans this wave
       // and the wave holding the other 32 rows (wave ^ gw).
       bool neg = true;
-      if (active) {
-        neg = (tmx == -INFINITY) || (m > 0.5f * kUnset && tmx - m < p.thr) || (q0 + n >= S);
-      }
+      if (active)
+        neg = (tmx == -INFINITY) || (m_true > 0.5f * kUnset && tmx - m_true < p.thr) ||
+              (q0 + n >= S);
       const bool all_neg = __all(neg);
       if (lane == 0) skip_flag[t & 1][wave] = all_neg ? 1 : 0;
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      block_barrier();
       skip_tile = active && all_neg && skip_flag[t & 1][wave ^ p.gw];
-      if (active && ((wave / p.gw) & 1) == 0 && lane == 0) {
-        const int qt = q0 / BN;
-        if (p.skip_map)
-          p.skip_map[(((size_t)b * p.Hq + head) * p.nT + qt) * p.nT + t] = skip_tile ? 1 : 0;
-        if (skip_tile && p.skip_count) atomicAdd(p.skip_count, 1ull);
+      if (active && ((wave / p.gw) & 1) == 0) {
+        if (lane == 0 && p.skip_map)
+          p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = skip_tile ? 1 : 0;
+        skipped += skip_tile ? 1u : 0u;
       }
+      if (active && !skip_tile) m_true = fmaxf(m_true, tmx);
     }
 
     if (active && !skip_tile) {
-      const float m_new = fmaxf(m, tmx);
-      const float alpha = fast_exp2(m - m_new);
-      const float nm = -m_new;
+      // lazy rescale: keep the exponent reference unless the row max grew
+      // by more than 8 (factor 256); exact either way after the final 1/l
+      if (__any(tmx > m_used + 8.f)) {
+        const float m_new = fmaxf(m_used, tmx);
+        const float alpha = fast_exp2(m_used - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        m_used = m_new;
+      }
+      const float nm = -m_used;
       uint32_t pk[2][8];
       float rs = 0.f;
 #pragma unroll
@@ -265,14 +339,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
           rs += p0 + p1;
           pk[kb][i >> 1] = pack_bf16(p0, p1);
         }
-      l = l * alpha + rs;
-      m = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      }
+      l += rs;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -280,27 +347,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
           const u32x4 pw = {pk[kb][kk * 4 + 0], pk[kb][kk * 4 + 1], pk[kb][kk * 4 + 2],
                             pk[kb][kk * 4 + 3]};
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-          const int lgrp = kb * 4 + kk * 2 + hf;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int d = db * 32 + n;
-            const int col = (lgrp ^ ((d >> 3) & 7)) << 3;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + d * T::VSTR + col);
+            const LDS_AS unsigned char* va = vl + v_base + (kb * 32 + kk * 16) * T::RV + db * 64;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)va);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(va + 8 * T::RV));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
           }
         }
     }
-
-    if (t + 1 < n_tiles) {
-      uint16_t* nk = smem + ((t + 1) & 1) * (T::KT + T::VT);
-      store_tile(nk, nk + T::KT);
-    }
-    __syncthreads();
   }
+
+  if (SKIP && lane == 0 && skipped && p.skip_count) atomicAdd(p.skip_count, (unsigned long long)skipped);
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = ln(sum) = (m + log2 l) ln 2
   if (!has_rows) return;
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = half_swap_add(l);
   const int row = q0 + n;
   if (row >= S) return;
   const float inv = 1.f / lt;
@@ -314,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
                  pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
       *reinterpret_cast<u32x2*>(orow + d0) = w;
     }
-  if (hf == 0 && p.lse) p.lse[qbase + row] = (m + __log2f(lt)) * kLn2;
+  if (hf == 0 && p.lse) p.lse[qbase + row] = (m_used + __log2f(lt)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool SKIP>
