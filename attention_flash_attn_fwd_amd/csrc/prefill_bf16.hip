@@ -41,6 +41,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -124,7 +126,7 @@ struct Tile {
   static constexpr int KT = BN * RK;          // = KSL KiB
   static constexpr int VT = BN * RV;          // = VSL KiB
   static constexpr int STAGE = KT + VT;
-  static constexpr int NST = 3;               // pipeline depth (tiles in flight)
+  static constexpr int NST = 4;               // LDS stages: t-1 (role B), t, t+1, t+2 in flight
   static constexpr size_t lds_bytes = (size_t)NST * STAGE;
   // DMA blocks issued by wave w per tile: blocks w, w+8, ... of KSL + VSL
   static __device__ __forceinline__ int dma_count(int w) {
@@ -145,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   __shared__ int skip_flag[2][kWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
 
   // ---- work item: heaviest query blocks first
@@ -173,20 +176,44 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   // One wave-wide load fills 1 KiB of LDS (16 bytes per lane, in lane
   // order); the lane fetches the global chunk that the swizzle puts there.
   // Keys past the end are clamped to the last key and masked later.
+  // Per-lane source offsets of this wave's DMA blocks within a tile: block
+  // i covers LDS slots 64i .. 64i+63, slot g = row g / SL, chunk g % SL (a
+  // pad slot re-reads chunk 0 of its row).  Fixed for every tile; the tile's
+  // first key enters through the scalar base address.
+  constexpr int NJK = (T::KSL + kWaves - 1) / kWaves, NJV = (T::VSL + kWaves - 1) / kWaves;
+  uint32_t koff[NJK], voff[NJV];
+  int krow[NJK], vrow[NJV];
+#pragma unroll
+  for (int j = 0; j < NJK; ++j) {
+    const int g = (wave + j * kWaves) * 64 + lane, c = g % T::KSL;
+    krow[j] = g / T::KSL;
+    koff[j] = (c < T::CH ? c : 0) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NJV; ++j) {
+    const int g = (wave + j * kWaves) * 64 + lane, c = g % T::VSL;
+    vrow[j] = g / T::VSL;
+    voff[j] = (c < T::CH ? c : 0) * 16;
+  }
   auto issue = [&](int t) {
     const uint32_t st = smem_base + (t % T::NST) * T::STAGE;
     const int key0 = t * BN;
+    const bool ragged = key0 + BN > S;  // clamp keys past the end to the last key
+    const uint16_t* kb_ = Kg + (size_t)key0 * D;
+    const uint16_t* vb_ = Vg + (size_t)key0 * D;
 #pragma unroll
-    for (int i = wave; i < T::KSL; i += kWaves) {
-      const int g = i * 64 + lane, r = g / T::KSL, c = g % T::KSL;
-      const uint32_t off = (uint32_t)min(key0 + r, S - 1) * T::RB + (c < T::CH ? c : 0) * 16;
-      dma16(Kg, off, st + i * 1024);
+    for (int j = 0; j < NJK; ++j) {
+      const int i = wave + j * kWaves;
+      if (i >= T::KSL) break;
+      const int r = ragged ? min(krow[j], S - 1 - key0) : krow[j];
+      dma16(kb_, (uint32_t)r * T::RB + koff[j], st + i * 1024);
     }
 #pragma unroll
-    for (int i = wave; i < T::VSL; i += kWaves) {
-      const int g = i * 64 + lane, r = g / T::VSL, c = g % T::VSL;
-      const uint32_t off = (uint32_t)min(key0 + r, S - 1) * T::RB + (c < T::CH ? c : 0) * 16;
-      dma16(Vg, off, st + T::KT + i * 1024);
+    for (int j = 0; j < NJV; ++j) {
+      const int i = wave + j * kWaves;
+      if (i >= T::VSL) break;
+      const int r = ragged ? min(vrow[j], S - 1 - key0) : vrow[j];
+      dma16(vb_, (uint32_t)r * T::RB + voff[j], st + T::KT + i * 1024);
     }
   };
   const int n_dma = T::dma_count(wave);
@@ -228,138 +255,164 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float m_used = kUnset;   // reference max of the exponentials (log2 units)
-  float m_true = kUnset;   // running max (block skip decisions)
+  float m_true = kUnset;   // running max over the tiles before the current one
   float l = 0.f;
   unsigned skipped = 0;
   const float sl2 = p.sl2;
+  const int first_masked = CAUSAL ? min(q0 / BN, S / BN) : S / BN;
 
-  int stage_off = 0;  // LDS offset of stage t % NST
+  // S^T of key tile t (raw scores) = K Q^T: two independent 32-key
+  // accumulator chains, operand reads running ahead of the MFMAs
+  auto qk = [&](int t, f32x16* sc) {
+    const LDS_AS unsigned char* kp = smem + (t % T::NST) * T::STAGE + k_base;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[0][i] = sc[1][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + ks * 32);
+      const bf16x8 a1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK + ks * 32);
+      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sc[0], 0, 0, 0);
+      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], sc[1], 0, 0, 0);
+    }
+    // 4 operand reads ahead, then alternate MFMA / read
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NKS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // mask (diagonal and ragged tiles only) and scaled row max of a score tile
+  auto row_max = [&](int t, f32x16* sc) -> float {
+    if (t >= first_masked) {
+      const int c0 = t * BN, qi = q0 + n;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = c0 + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+          if (key >= S || (CAUSAL && key > qi)) sc[kb][i] = -INFINITY;
+        }
+    }
+    float m0 = fmaxf(sc[0][0], sc[1][0]), m1 = fmaxf(sc[0][1], sc[1][1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) {
+      m0 = fmaxf(fmaxf(m0, sc[0][i]), sc[1][i]);
+      m1 = fmaxf(fmaxf(m1, sc[0][i + 1]), sc[1][i + 1]);
+    }
+    return half_swap_max(fmaxf(m0, m1)) * sl2;
+  };
+  // softmax of a score tile and O^T += V^T P^T for key tile t.  The
+  // exponent reference moves (with a rescale of O and l) only when the row
+  // max grew by more than 8, a factor 256; the result is exact after 1/l.
+  auto finish = [&](int t, f32x16* sc, float tmx) {
+    if (__any(tmx > m_used + 8.f)) {
+      const float m_new = fmaxf(m_used, tmx);
+      const float alpha = fast_exp2(m_used - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m_used = m_new;
+    }
+    const float nm = -m_used;
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2)
+        pk[kb][i >> 1] = pack_bf16(fast_exp2(fmaf(sc[kb][i], sl2, nm)),
+                                   fast_exp2(fmaf(sc[kb][i + 1], sl2, nm)));
+    // row sum of the bf16-rounded P (the values P.V uses), two per dot2
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[0][j]), kOnes2, rs0, false);
+      rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[1][j]), kOnes2, rs1, false);
+    }
+    l += rs0 + rs1;
+    const LDS_AS unsigned char* vl = smem + (t % T::NST) * T::STAGE + T::KT + v_base;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 pw = {pk[kb][kk * 4 + 0], pk[kb][kk * 4 + 1], pk[kb][kk * 4 + 2],
+                          pk[kb][kk * 4 + 3]};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const LDS_AS unsigned char* va = vl + (kb * 32 + kk * 16) * T::RV + db * 64;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)va);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(va + 8 * T::RV));
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+        }
+      }
+  };
+  // block-skip vote of this wave's 32 rows for key tile t, published in LDS
+  auto publish_vote = [&](int t, float tmx_t) {
+    bool neg = true;
+    if (t < wave_tiles)
+      neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < p.thr) ||
+            (q0 + n >= S);
+    const bool all_neg = __all(neg);
+    if (lane == 0) skip_flag[t & 1][wave] = all_neg ? 1 : 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // read the pair's votes for tile t; record the decision; true if skipped
+  auto decide = [&](int t) -> bool {
+    const bool sk = skip_flag[t & 1][wave] && skip_flag[t & 1][wave ^ p.gw];
+    if (((wave / p.gw) & 1) == 0) {
+      if (lane == 0 && p.skip_map)
+        p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = sk ? 1 : 0;
+      skipped += sk ? 1u : 0u;
+    }
+    return sk;
+  };
+
+  // The two waves sharing a SIMD (w and w+4) run the tile loop out of phase
+  // so that one's softmax VALU work overlaps the other's MFMAs: role A does
+  // Q.K^T, softmax and P.V of tile t; role B finishes tile t-1 (softmax,
+  // P.V) and then computes Q.K^T of tile t.  The block-skip decision needs
+  // both halves of a 64-row tile first, so with block skip every wave is B.
+  const bool role_b = SKIP || ((wave >> 2) & 1);
+  f32x16 sc[2];
+  float tmx_prev = -INFINITY;
   for (int t = 0; t < n_tiles; ++t) {
     if (t + 1 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
     block_barrier();
     if (t + 2 < n_tiles) issue(t + 2);
-    const LDS_AS unsigned char* kl = smem + stage_off;
-    stage_off = stage_off == (T::NST - 1) * T::STAGE ? 0 : stage_off + T::STAGE;
-    const LDS_AS unsigned char* vl = kl + T::KT;
-    const bool active = t < wave_tiles;
-    const int c0 = t * BN;
-
-    f32x16 s[2];
-    float tmx = -INFINITY;
-    if (active) {
-      // two independent accumulator chains (key rows 0-31 and 32-63); the
-      // operand reads run one k-step ahead of the MFMAs
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.f;
-      const LDS_AS unsigned char* kp = kl + k_base;
-      bf16x8 a0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp);
-      bf16x8 a1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (ks + 1 < NKS) {
-          n0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + (ks + 1) * 32);
-          n1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK + (ks + 1) * 32);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s[1], 0, 0, 0);
-        a0 = n0;
-        a1 = n1;
-      }
-      // schedule: 4 operand reads ahead, then alternate MFMA / read
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * NKS - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      const bool need_mask = (c0 + BN > S) || (CAUSAL && c0 + BN - 1 > q0);
-      if (need_mask) {
-        const int qi = q0 + n;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = c0 + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-            if (key >= S || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
-          }
-      }
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      tmx = half_swap_max(mx) * sl2;
+    // role B: finish tile t-1
+    if (role_b && t >= 1 && t - 1 < wave_tiles) {
+      bool sk = false;
+      if constexpr (SKIP) sk = decide(t - 1);
+      if (!sk) finish(t - 1, sc, tmx_prev);
+      m_true = fmaxf(m_true, tmx_prev);
     }
-
-    bool skip_tile = false;
-    if constexpr (SKIP) {
-      // BLASST test for this wave's 32 rows; the 64-row tile spans this wave
-      // and the wave holding the other 32 rows (wave ^ gw).
-      bool neg = true;
-      if (active)
-        neg = (tmx == -INFINITY) || (m_true > 0.5f * kUnset && tmx - m_true < p.thr) ||
-              (q0 + n >= S);
-      const bool all_neg = __all(neg);
-      if (lane == 0) skip_flag[t & 1][wave] = all_neg ? 1 : 0;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      block_barrier();
-      skip_tile = active && all_neg && skip_flag[t & 1][wave ^ p.gw];
-      if (active && ((wave / p.gw) & 1) == 0) {
-        if (lane == 0 && p.skip_map)
-          p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = skip_tile ? 1 : 0;
-        skipped += skip_tile ? 1u : 0u;
-      }
-      if (active && !skip_tile) m_true = fmaxf(m_true, tmx);
+    // both roles: scores of tile t
+    if (t < wave_tiles) {
+      qk(t, sc);
+      tmx_prev = row_max(t, sc);
     }
-
-    if (active && !skip_tile) {
-      // lazy rescale: keep the exponent reference unless the row max grew
-      // by more than 8 (factor 256); exact either way after the final 1/l
-      if (__any(tmx > m_used + 8.f)) {
-        const float m_new = fmaxf(m_used, tmx);
-        const float alpha = fast_exp2(m_used - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        m_used = m_new;
-      }
-      const float nm = -m_used;
-      uint32_t pk[2][8];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(s[kb][i], sl2, nm));
-          const float p1 = fast_exp2(fmaf(s[kb][i + 1], sl2, nm));
-          rs += p0 + p1;
-          pk[kb][i >> 1] = pack_bf16(p0, p1);
-        }
-      l += rs;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 pw = {pk[kb][kk * 4 + 0], pk[kb][kk * 4 + 1], pk[kb][kk * 4 + 2],
-                            pk[kb][kk * 4 + 3]};
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const LDS_AS unsigned char* va = vl + v_base + (kb * 32 + kk * 16) * T::RV + db * 64;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)va);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(va + 8 * T::RV));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
-          }
-        }
+    // role A: finish tile t
+    if (!role_b && t < wave_tiles) finish(t, sc, tmx_prev);
+    if constexpr (SKIP) publish_vote(t, tmx_prev);
+  }
+  if (role_b) {
+    if constexpr (SKIP) block_barrier();
+    const int t = n_tiles - 1;
+    if (t < wave_tiles) {
+      bool sk = false;
+      if constexpr (SKIP) sk = decide(t);
+      if (!sk) finish(t, sc, tmx_prev);
     }
   }
 
-  if (SKIP && lane == 0 && skipped && p.skip_count) atomicAdd(p.skip_count, (unsigned long long)skipped);
+  if (SKIP && lane == 0 && skipped && p.skip_count)
+    atomicAdd(p.skip_count, (unsigned long long)skipped);
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = ln(sum) = (m + log2 l) ln 2
   if (!has_rows) return;
