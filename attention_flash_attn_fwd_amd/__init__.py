@@ -66,8 +66,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
     lib.attn_decode_paged.restype = _I
-    lib.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _F,
-                                      _P, ctypes.c_size_t, _P]
+    lib.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                      _F, _P, ctypes.c_size_t, _P]
     _LIB = lib
     return lib
 
@@ -175,13 +175,26 @@ def attn_decode_workspace_bytes(num_seqs: int, Hq: int, D: int, max_blocks_per_s
                                                   block_size))
 
 
+KV_LAYOUTS = {"rowmajor": 0, "mfma": 1}
+
+
+def _pool_shapes(NB, Hkv, bs, D, layout):
+    if layout == "rowmajor":
+        return (NB, Hkv, bs, D), (NB, Hkv, bs, D)
+    return (NB, Hkv, D // 8, bs, 8), (NB, Hkv, D, bs)
+
+
 def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o, lse,
-                      scale: float, workspace, stream=None) -> None:
-    """Paged decode into caller-allocated o [N,Hq,D] and lse [N,Hq] (or None)."""
+                      scale: float, workspace, stream=None, layout: str = "rowmajor") -> None:
+    """Paged decode into caller-allocated o [N,Hq,D] and lse [N,Hq] (or None).
+    ``layout`` names the pool layout: "rowmajor" or "mfma" (see include/attn.h)."""
     N, Hq, D = q.shape
-    NB, Hkv, bs, Dk = k_pool.shape
+    NB, Hkv = k_pool.shape[0], k_pool.shape[1]
     _dev(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace)
-    if Dk != D or bs != block_size or v_pool.shape != k_pool.shape or o.shape != q.shape:
+    if layout not in KV_LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
+    ks, vs = _pool_shapes(NB, Hkv, block_size, D, layout)
+    if tuple(k_pool.shape) != ks or tuple(v_pool.shape) != vs or o.shape != q.shape:
         raise ValueError("shape mismatch")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
@@ -191,7 +204,8 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int,
         raise ValueError("lse must be float32 [N,Hq]")
     nbytes = workspace.numel() * workspace.element_size()
     st = load().attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                  _ptr(seq_lens), int(block_size), _ptr(o), _ptr(lse), N, Hq, Hkv,
+                                  _ptr(seq_lens), int(block_size), KV_LAYOUTS[layout], _ptr(o),
+                                  _ptr(lse), N, Hq, Hkv,
                                   D, NB, int(block_table.shape[1]), float(scale), _ptr(workspace),
                                   nbytes, _stream(stream))
     _check(st, "attn_decode_paged")
@@ -230,7 +244,7 @@ def prefill_blockskip(q, k, v, scale: Optional[float] = None, lam: float = 1e-3,
 
 
 def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int = 16,
-                 scale: Optional[float] = None, workspace=None):
+                 scale: Optional[float] = None, workspace=None, layout: str = "rowmajor"):
     """Allocate O, LSE (and the workspace unless given) and run the paged decode."""
     N, Hq, D = q.shape
     if scale is None:
@@ -241,5 +255,5 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int = 16,
         nbytes = attn_decode_workspace_bytes(N, Hq, D, int(block_table.shape[1]), block_size)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse, scale,
-                      workspace)
+                      workspace, layout=layout)
     return o, lse

@@ -116,7 +116,7 @@ size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_blocks_p
 
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                      void* o, float* lse, int num_seqs, int Hq, int Hkv, int D, int num_blocks,
+                      int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D, int num_blocks,
                       int max_blocks_per_seq, float scale, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
@@ -124,6 +124,7 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
     return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (!finite_pos(scale)) return ATTN_ERR_INVALID_ARG;
+  if (kv_layout != ATTN_KV_ROWMAJOR && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_INVALID_ARG;
   if (block_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
@@ -151,6 +152,7 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   a.block_size = block_size;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
+  a.layout = kv_layout;
   a.scale = scale;
   a.n_split = ns;
   a.ws_o = static_cast<float*>(workspace);

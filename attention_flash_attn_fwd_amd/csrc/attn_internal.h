@@ -38,6 +38,7 @@ struct DecodeArgs {
   void* o;
   float* lse;  // may be null
   int N, Hq, Hkv, D, block_size, num_blocks, max_blocks;
+  int layout;  // 0 row-major pools, 1 MFMA-native pools
   float scale;
   float* ws_o;    // [N, Hq, n_split, D]
   float* ws_lse;  // [N, Hq, n_split]

@@ -6,20 +6,23 @@
 // a sequence's logical blocks to non-contiguous physical ones, like an OS
 // page table; "TensorRT-LLM：大模型推理加速的工业级引擎", PagedAttention).
 // Small-batch decode is bound by reading the KV cache from HBM (same page,
-// decode stage), so the kernel is built around moving K/V at full bandwidth:
-//  * A workgroup (4 waves) owns one (sequence, K/V head, 256-token split).
-//    All Hq/Hkv query heads of the K/V head are handled together, so each
-//    K/V byte is read from HBM exactly once (the GQA saving of the
+// decode stage), so the kernel is built around keeping K/V reads in flight:
+//  * A workgroup is one wave and owns one (sequence, K/V head, 256-token
+//    split).  The G = Hq/Hkv query heads of the K/V head are processed
+//    together, so each K/V byte is read from HBM once (the GQA saving of the
 //    "TensorRT对Grouped Query Attention的支持进展" page, 技术演进背景).
-//  * Each wave walks 4 of the split's 16-token blocks.  A pool block of one
-//    head is a contiguous 4 KiB run ([block, head, slot, dim] layout), read
-//    with 16-byte loads: lane = (token row, 8-dim chunk), fully coalesced.
-//  * Scores: per lane partial dot products over its 8 dims for every head,
-//    summed across the chunk lanes with DPP; online softmax in base 2.
-//  * P.V accumulates per lane over its own rows; rows and waves are combined
-//    once per split.  The split's (O / l, log2-sum-exp) goes to the caller's
-//    workspace; the merge kernel combines splits with
-//    lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
+//  * The split is walked in tiles of 32 tokens (two pool blocks).  A pool
+//    block of one head is a contiguous 4 KiB run ([block, head, slot, dim]);
+//    it is copied into LDS with asynchronous 16-byte-per-lane DMA (one scalar
+//    base per block from the block table), double buffered, with the 16-byte
+//    chunks of each row XOR-permuted so that the operand reads below are
+//    bank-conflict free.
+//  * S^T = K Q^T and O^T += V^T P^T use v_mfma_f32_16x16x32_bf16 with the
+//    query heads as the 16-wide N dimension (G <= 16); V^T comes from the
+//    transposing LDS read.  Softmax is online, in base 2.
+//  * The split's (O / l, log2-sum-exp) goes to the caller's workspace; the
+//    merge kernel combines the splits: lse = log sum_s exp(lse_s),
+//    O = sum_s exp(lse_s - lse) O_s.
 #include "attn_internal.h"
 
 #include <math.h>
@@ -27,15 +30,18 @@
 namespace attn {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kBlk = 16;  // tokens per pool block
-constexpr int kBlocksPerSplit = kDecodeSplitTokens / kBlk;
-constexpr int kBlocksPerWave = kBlocksPerSplit / kDecWaves;
+constexpr int kTT = 32;   // tokens per tile (two blocks)
 constexpr float kUnset = -1e30f;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct DecParams {
   const uint16_t* q;
@@ -47,180 +53,401 @@ struct DecParams {
   float* lse;
   float* ws_o;
   float* ws_lse;
-  int Hq, Hkv, num_blocks, max_blocks, n_split;
+  int Hq, Hkv, G, num_blocks, max_blocks, n_split;
   float sl2;
 };
 
-__device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  f2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2));  // RNE
 }
 
-// Sum over the CH consecutive lanes that hold one token row (CH = 8 or 16);
-// every one of those lanes ends with the total.
-template <int CH>
-__device__ __forceinline__ float row_sum(float x) {
-  if constexpr (CH == 16) x += dpp<0x128>(x);  // row_ror:8
-  x += dpp<0x141>(x);                           // row_half_mirror
-  x += dpp<0xB1>(x);                            // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);                            // quad_perm [2,3,0,1]
-  return x;
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes at gbase + voff land at LDS byte lds_addr + 16*i.  Issued
+// from asm so that the compiler does not serialise it against unrelated LDS
+// reads; completion is awaited explicitly with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(gbase), "s"(m) : "memory");
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecParams p) {
-  constexpr int CH = D / 8;       // 16-byte chunks per token row
-  constexpr int RPL = 64 / CH;    // token rows covered by one wave-wide load
-  constexpr int LPB = kBlk / RPL; // loads per 16-token block
-  __shared__ float sm_m[kDecWaves][G];
-  __shared__ float sm_l[kDecWaves][G];
-  __shared__ float sm_o[kDecWaves][G][D];
-  __shared__ int sm_err;
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS tile: 32 rows (tokens) of D bf16, 16-byte chunk c of row r stored at
+// slot c ^ swz(r).  K is read as 16-byte MFMA A fragments (16 rows, same
+// chunk), V with the transposing 8-byte read (8 rows x 32 bytes per half
+// wave); the XOR patterns spread both over all 64 banks.
+template <int D>
+struct DTile {
+  static constexpr int RB = D * 2;             // bytes per row
+  static constexpr int TB = kTT * RB;          // bytes per K (or V) tile
+  static constexpr int NI = TB / 1024;         // DMA instructions per tensor per tile
+  static constexpr int RPI = 1024 / RB;        // rows per DMA instruction
+  static constexpr int NST = 2;                // stages (tiles resident or in flight)
+  static constexpr int LDS = NST * 2 * TB;
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
+  using T = DTile<D>;
+  constexpr int NKS = D / 32;   // 32-dim k-steps of Q.K^T
+  constexpr int NDB = D / 16;   // 16-dim output blocks of P.V
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[T::LDS];
+  LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
   const int split = blockIdx.x, kvh = blockIdx.y, n = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane / CH, c = lane % CH;
+  const int lane = threadIdx.x;
+  const int h = lane & 15, g4 = lane >> 4;
   const int L = p.seq_lens[n];
-  if (L <= 0 || split * kDecodeSplitTokens >= L) return;  // merge handles L <= 0
-  if (tid == 0) sm_err = 0;
-  __syncthreads();
+  const int tok_begin = split * kDecodeSplitTokens;
+  if (L <= 0 || tok_begin >= L) return;  // the merge kernel handles L <= 0
+  const int n_tok = min(L - tok_begin, kDecodeSplitTokens);
+  const int n_tiles = (n_tok + kTT - 1) / kTT;
+  const int G = p.G;
 
-  // q for the G heads of this K/V head, dims c*8..c*8+7, pre-scaled to log2 units
-  float qf[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(
-        p.q + ((size_t)n * p.Hq + kvh * G + h) * D + c * 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qf[h][2 * j] = lo_bf16(w[j]) * p.sl2;
-      qf[h][2 * j + 1] = hi_bf16(w[j]) * p.sl2;
-    }
-  }
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kUnset;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-  bool err = false;
+  // The split's block-table entries, one per lane (lanes < n_blk), fetched
+  // together with Q in a single round trip.  A bad entry or a length past
+  // the table end poisons the whole sequence with NaN.
   const int32_t* trow = p.table + (size_t)n * p.max_blocks;
+  const int lb0 = tok_begin / kBlk;
+  const int n_blk = (n_tok + kBlk - 1) / kBlk;
+  const bool in_table = lb0 + n_blk <= p.max_blocks;
+  int my_ph = 0;
+  if (in_table && lane < n_blk) my_ph = trow[lb0 + lane];
+  // Q^T as the B operand: lane (head h, group g4) holds dims ks*32 + g4*8 .. +7
+  bf16x8 qB[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (h < G)
+      qB[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)n * p.Hq + kvh * G + h) * D +
+                                                ks * 32 + g4 * 8);
+    else
+      qB[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
+  const bool lane_ok = lane >= n_blk || (my_ph >= 0 && my_ph < p.num_blocks);
+  const bool bad = !in_table || !__all(lane_ok);
+  const size_t slot = ((size_t)n * p.Hq + kvh * G + h) * p.n_split + split;
+  if (bad) {
+    if (h < G) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = f32x4{NAN, NAN, NAN, NAN};
+      if (g4 == 0) p.ws_lse[slot] = NAN;
+    }
+    return;
+  }
 
-  for (int jj = 0; jj < kBlocksPerWave; ++jj) {
-    const int lb = split * kBlocksPerSplit + wave * kBlocksPerWave + jj;
-    const int tok0 = lb * kBlk;
-    if (tok0 >= L) break;
-    if (lb >= p.max_blocks) { err = true; break; }
-    const int phys = trow[lb];
-    if (phys < 0 || phys >= p.num_blocks) { err = true; break; }
-    const size_t base = (((size_t)phys * p.Hkv + kvh) * kBlk) * D + c * 8;
-    u32x4 kr[LPB], vr[LPB];
+  const size_t head_stride = (size_t)kBlk * T::RB;             // bytes of one (block, head)
+  const size_t blk_stride = (size_t)p.Hkv * head_stride;       // bytes of one pool block
+  const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k_pool) + kvh * head_stride;
+  const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v_pool) + kvh * head_stride;
+
+  // DMA of tile t into stage t % NST.  Rows past the sequence end re-read its
+  // last token, so every LDS row holds finite data (tail slots of the last
+  // pool block may hold anything).
+  auto issue = [&](int t) {
+    const uint32_t st = smem_base + (t % T::NST) * 2 * T::TB;
+    const int v = min(kTT, n_tok - t * kTT);   // valid rows of this tile
+    const int ph0 = __builtin_amdgcn_readlane(my_ph, 2 * t);
+    const int ph1 = v > kBlk ? __builtin_amdgcn_readlane(my_ph, 2 * t + 1) : ph0;
 #pragma unroll
-    for (int rr = 0; rr < LPB; ++rr) {
-      const int tok = rr * RPL + r;
-      kr[rr] = *reinterpret_cast<const u32x4*>(p.k_pool + base + (size_t)tok * D);
-      vr[rr] = *reinterpret_cast<const u32x4*>(p.v_pool + base + (size_t)tok * D);
+    for (int i = 0; i < T::NI; ++i) {
+      const int row0 = i * T::RPI;
+      const int bi = (row0 >= kBlk && v > kBlk) ? 1 : 0;   // block supplying these rows
+      const int ph = bi ? ph1 : ph0;
+      const int row = row0 + (lane * 16) / T::RB;
+      const int slotc = ((lane * 16) % T::RB) / 16;
+      const int src = min(row, v - 1) - bi * kBlk;          // row within the block
+      const uint32_t ko = (uint32_t)src * T::RB + ((slotc ^ T::swz_k(row)) << 4);
+      const uint32_t vo = (uint32_t)src * T::RB + ((slotc ^ T::swz_v(row)) << 4);
+      dma16(kpool + (size_t)ph * blk_stride, ko, st + i * 1024);
+      dma16(vpool + (size_t)ph * blk_stride, vo, st + T::TB + i * 1024);
     }
-    float s[G][LPB];
+  };
+
+  f32x4 acc[NDB];
 #pragma unroll
-    for (int rr = 0; rr < LPB; ++rr) {
-      float kf[8];
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_used = kUnset, l = 0.f;
+  const float sl2 = p.sl2;
+  // per-lane LDS offsets: K fragment (row h of block b, chunk 4ks + g4);
+  // V^T fragment source (rows base + s/4, dims d0 + 4(s%4))
+  const int vs = lane & 15;
+  const int v_row0 = 4 * g4 + (vs >> 2);
+
+  for (int t = 0; t < min(n_tiles, T::NST - 1); ++t) issue(t);
+  // wait until tile t has landed, given how many later tiles are in flight
+  auto wait_tile = [&](int later) {
+    switch (later) {
+      case 0: wait_vmem<0>(); break;
+      case 1: wait_vmem<2 * T::NI>(); break;
+      case 2: wait_vmem<4 * T::NI>(); break;
+      default: wait_vmem<6 * T::NI>(); break;
+    }
+  };
+  for (int t = 0; t < n_tiles; ++t) {
+    // stage (t-1) % NST was fully read at the end of the previous iteration
+    if (t + T::NST - 1 < n_tiles) issue(t + T::NST - 1);
+    wait_tile(min(t + T::NST - 1, n_tiles - 1) - t);
+    asm volatile("" ::: "memory");
+    const LDS_AS unsigned char* kl = smem + (t % T::NST) * 2 * T::TB;
+    const LDS_AS unsigned char* vl = kl + T::TB;
+
+    // scores S^T (32 tokens x 16 heads): lane (h, g4) gets tokens b*16 + 4*g4 + i
+    f32x4 s[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kf[2 * j] = lo_bf16(kr[rr][j]);
-        kf[2 * j + 1] = hi_bf16(kr[rr][j]);
-      }
-      const bool valid = tok0 + rr * RPL + r < L;
-      // slots past the sequence end hold arbitrary bits (even NaN): drop them
-      // from P.V as well, since 0 * NaN would poison the accumulator
-      if (!valid) vr[rr] = u32x4{0, 0, 0, 0};
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = b * 16 + h;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[e], d);
-        d = row_sum<CH>(d);
-        s[h][rr] = valid ? d : -INFINITY;
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c = 4 * ks + g4;
+        const bf16x8 a =
+            *reinterpret_cast<const LDS_AS bf16x8*>(kl + row * T::RB + ((c ^ T::swz_k(row)) << 4));
+        s[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[ks], s[b], 0, 0, 0);
       }
     }
+    const int valid = n_tok - t * kTT;
+    if (valid < kTT) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float bm = s[h][0];
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int rr = 1; rr < LPB; ++rr) bm = fmaxf(bm, s[h][rr]);
+        for (int i = 0; i < 4; ++i)
+          if (b * 16 + 4 * g4 + i >= valid) s[b][i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    const float tmx = half_swap_max(mx) * sl2;
+    if (__any(tmx > m_used + 8.f)) {  // lazy rescale (exponent reference moves by > 2^8)
+      const float m_new = fmaxf(m_used, tmx);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+      l *= alpha;
 #pragma unroll
-      for (int x = CH; x < 64; x <<= 1) bm = fmaxf(bm, __shfl_xor(bm, x));
-      const float m_new = fmaxf(m[h], bm);
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
-      m[h] = m_new;
-      float pr[LPB];
-      float ps = 0.f;
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float nm = -m_used;
+    // packed bf16 P^T (B operand): slots j<4 are tokens 4*g4+j of block 0,
+    // slots j>=4 tokens 4*g4+j-4 of block 1.  Kept as a plain array: the
+    // row-sum dot products below must see the four words separately.
+    uint32_t pk[4];
 #pragma unroll
-      for (int rr = 0; rr < LPB; ++rr) {
-        pr[rr] = __builtin_amdgcn_exp2f(s[h][rr] - m_new);
-        ps += pr[rr];
+    for (int b = 0; b < 2; ++b) {
+      pk[2 * b] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[b][0], sl2, nm)),
+                            __builtin_amdgcn_exp2f(fmaf(s[b][1], sl2, nm)));
+      pk[2 * b + 1] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[b][2], sl2, nm)),
+                                __builtin_amdgcn_exp2f(fmaf(s[b][3], sl2, nm)));
+    }
+    float rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[0]), kOnes2, 0.f, false);
+    float rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[1]), kOnes2, 0.f, false);
+    rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[2]), kOnes2, rs0, false);
+    rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[3]), kOnes2, rs1, false);
+    l += rs0 + rs1;
+    const u32x4 pw = {pk[0], pk[1], pk[2], pk[3]};
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    // O^T += V^T P^T: V^T rows d = db*16 + lane%16, token slots 8*g4 + j
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + 4 * (vs & 3);
+      const int c = d >> 3;
+      const int r0 = v_row0, r1 = 16 + v_row0;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(vl + r0 * T::RB + ((c ^ T::swz_v(r0)) << 4) + (d & 7) * 2));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(vl + r1 * T::RB + ((c ^ T::swz_v(r1)) << 4) + (d & 7) * 2));
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[db], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage t fully read
+  }
+
+  // combine the four lanes of each head and write the split's partial result
+  float lt = l + __shfl_xor(l, 16);
+  lt = half_swap_add(lt);
+  if (h < G) {
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = acc[db] * inv;
+    if (g4 == 0) p.ws_lse[slot] = m_used + __log2f(lt);
+  }
+}
+
+// Decode over a pool in the MFMA-native layout: inside each (block, head)
+// run, K is stored as 8-element chunks, chunk-major ([D/8][16][8]), and V is
+// stored transposed ([D][16]).  Every MFMA operand is then one plain vector
+// load from HBM with no LDS staging:
+//  * S^T = K Q^T (v_mfma_f32_16x16x32_bf16): lane (token t = lane%16,
+//    group g = lane/16) loads chunk 4*ks + g of token t, 16 bytes; the 64
+//    lanes of one load cover 1 KiB contiguously.
+//  * O^T += V^T P^T (v_mfma_f32_16x16x16_bf16): lane (dim d = lane%16 +
+//    16*db, group g) loads V^T[d][4g .. 4g+3], 8 bytes; 512 contiguous bytes
+//    per load.  Its k-slots are exactly the keys the S^T accumulator gives
+//    the same lane, so P^T needs no shuffle.
+// Loads run two blocks ahead of the MFMAs; occupancy is high because no LDS
+// is used, which keeps many K/V bytes in flight.
+template <int D>
+__global__ __launch_bounds__(64) void decode_native_kernel(DecParams p) {
+  constexpr int NKS = D / 32;  // 32-dim k-steps of Q.K^T
+  constexpr int NDB = D / 16;  // 16-dim output blocks of P.V
+  constexpr int RUN = kBlk * D * 2;  // bytes of one (block, head) run
+
+  const int split = blockIdx.x, kvh = blockIdx.y, n = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int h = lane & 15, g4 = lane >> 4;
+  const int L = p.seq_lens[n];
+  const int tok_begin = split * kDecodeSplitTokens;
+  if (L <= 0 || tok_begin >= L) return;  // the merge kernel handles L <= 0
+  const int n_tok = min(L - tok_begin, kDecodeSplitTokens);
+  const int G = p.G;
+
+  const int32_t* trow = p.table + (size_t)n * p.max_blocks;
+  const int lb0 = tok_begin / kBlk;
+  const int n_blk = (n_tok + kBlk - 1) / kBlk;
+  const bool in_table = lb0 + n_blk <= p.max_blocks;
+  int my_ph = 0;
+  if (in_table && lane < n_blk) my_ph = trow[lb0 + lane];
+  bf16x8 qB[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (h < G)
+      qB[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)n * p.Hq + kvh * G + h) * D +
+                                                ks * 32 + g4 * 8);
+    else
+      qB[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  const bool lane_ok = lane >= n_blk || (my_ph >= 0 && my_ph < p.num_blocks);
+  const bool bad = !in_table || !__all(lane_ok);
+  const size_t slot = ((size_t)n * p.Hq + kvh * G + h) * p.n_split + split;
+  if (bad) {
+    if (h < G) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = f32x4{NAN, NAN, NAN, NAN};
+      if (g4 == 0) p.ws_lse[slot] = NAN;
+    }
+    return;
+  }
+
+  const size_t blk_stride = (size_t)p.Hkv * RUN;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k_pool) + (size_t)kvh * RUN;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v_pool) + (size_t)kvh * RUN;
+  const uint32_t k_off = (uint32_t)((g4 * 16 + h) * 16);       // + ks * 1024
+  const uint32_t v_off = (uint32_t)((h * 16 + 4 * g4) * 2);    // + db * 512
+
+  struct Buf {
+    bf16x8 k[NKS];
+    s16x4 v[NDB];
+  };
+  auto load = [&](int j, Buf& b) {
+    const size_t ph = (size_t)__builtin_amdgcn_readlane(my_ph, j);
+    const unsigned char* kb = kbase + ph * blk_stride + k_off;
+    const unsigned char* vb = vbase + ph * blk_stride + v_off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) b.k[ks] = *reinterpret_cast<const bf16x8*>(kb + ks * 1024);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) b.v[db] = *reinterpret_cast<const s16x4*>(vb + db * 512);
+  };
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_used = kUnset, l = 0.f;
+  const float sl2 = p.sl2;
+
+  auto compute = [&](int j, Buf& b) {
+    // scores S^T (16 tokens x 16 heads): lane (h, g4) gets tokens 4*g4 + i
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b.k[ks], qB[ks], s, 0, 0, 0);
+    const int valid = n_tok - j * kBlk;
+    if (valid < kBlk) {
+      // slots past the sequence end: no score, and their V (arbitrary bits,
+      // possibly NaN) must not reach P.V, where 0 * NaN would poison O
+      uint32_t keep[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g4 + i >= valid) s[i] = -INFINITY;
+      keep[0] = (4 * g4 + 0 < valid ? 0xffffu : 0u) | (4 * g4 + 1 < valid ? 0xffff0000u : 0u);
+      keep[1] = (4 * g4 + 2 < valid ? 0xffffu : 0u) | (4 * g4 + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 w = __builtin_bit_cast(u32x2, b.v[db]);
+        w[0] &= keep[0];
+        w[1] &= keep[1];
+        b.v[db] = __builtin_bit_cast(s16x4, w);
       }
-      l[h] = l[h] * alpha + ps;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    const float tmx = half_swap_max(mx) * sl2;
+    if (__any(tmx > m_used + 8.f)) {  // lazy rescale (exponent reference moves by > 2^8)
+      const float m_new = fmaxf(m_used, tmx);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+      l *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float nm = -m_used;
+    const uint32_t pk0 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[0], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[1], sl2, nm)));
+    const uint32_t pk1 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[2], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[3], sl2, nm)));
+    l += __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk0), kOnes2, 0.f, false) +
+         __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk1), kOnes2, 0.f, false);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 pw = {pk0, pk1};
+    const s16x4 pB = __builtin_bit_cast(s16x4, pw);
 #pragma unroll
-      for (int rr = 0; rr < LPB; ++rr) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[h][2 * j] = fmaf(pr[rr], lo_bf16(vr[rr][j]), acc[h][2 * j]);
-          acc[h][2 * j + 1] = fmaf(pr[rr], hi_bf16(vr[rr][j]), acc[h][2 * j + 1]);
-        }
-      }
+    for (int db = 0; db < NDB; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(b.v[db], pB, acc[db], 0, 0, 0);
+  };
+
+  // two buffers, loads two blocks ahead of the MFMAs
+  Buf b0, b1;
+  load(0, b0);
+  if (n_blk > 1) load(1, b1);
+  for (int j = 0; j < n_blk; j += 2) {
+    compute(j, b0);
+    if (j + 2 < n_blk) load(j + 2, b0);
+    if (j + 1 < n_blk) {
+      compute(j + 1, b1);
+      if (j + 3 < n_blk) load(j + 3, b1);
     }
   }
 
-  // combine the token rows of this wave (lanes with equal chunk c)
+  float lt = l + __shfl_xor(l, 16);
+  lt = half_swap_add(lt);
+  if (h < G) {
+    const float inv = 1.f / lt;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int x = CH; x < 64; x <<= 1) {
-      l[h] += __shfl_xor(l[h], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], x);
-    }
-  }
-  if (err) atomicOr(&sm_err, 1);
-  if (lane < CH) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][h][c * 8 + e] = acc[h][e];
-      if (lane == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-
-  // combine the waves and write this split's normalised partial result
-  const bool bad = sm_err != 0;
-  for (int it = tid; it < G * D; it += kDecThreads) {
-    const int h = it / D, d = it % D;
-    float M = kUnset;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float Lsum = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
-      Lsum += sc * sm_l[w][h];
-      O += sc * sm_o[w][h][d];
-    }
-    const size_t slot = ((size_t)n * p.Hq + kvh * G + h) * p.n_split + split;
-    p.ws_o[slot * D + d] = bad ? NAN : O / Lsum;
-    if (d == 0) p.ws_lse[slot] = bad ? NAN : M + __log2f(Lsum);
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = acc[db] * inv;
+    if (g4 == 0) p.ws_lse[slot] = m_used + __log2f(lt);
   }
 }
 
@@ -268,22 +495,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
   if (d == 0 && p.lse) p.lse[out] = bad ? NAN : (M + __log2f(W)) * kLn2;
 }
 
-template <int D, int G>
-void launch_split(const DecParams& p, int N, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(p.n_split, p.Hkv, N), dim3(kDecThreads),
-                     0, stream, p);
-}
-
 template <int D>
-hipError_t launch_d(const DecParams& p, int N, int G, hipStream_t stream) {
-  switch (G) {
-    case 1: launch_split<D, 1>(p, N, stream); break;
-    case 2: launch_split<D, 2>(p, N, stream); break;
-    case 4: launch_split<D, 4>(p, N, stream); break;
-    case 8: launch_split<D, 8>(p, N, stream); break;
-    case 16: launch_split<D, 16>(p, N, stream); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_d(const DecParams& p, int N, int layout, hipStream_t stream) {
+  if (layout == 1)
+    hipLaunchKernelGGL((decode_native_kernel<D>), dim3(p.n_split, p.Hkv, N), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(p.n_split, p.Hkv, N), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.Hq, N), dim3(D), 0, stream, p);
@@ -309,8 +526,9 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.max_blocks = a.max_blocks;
   p.n_split = a.n_split;
   p.sl2 = a.scale * 1.4426950408889634f;
-  const int G = a.Hq / a.Hkv;
-  return a.D == 64 ? launch_d<64>(p, a.N, G, stream) : launch_d<128>(p, a.N, G, stream);
+  p.G = a.Hq / a.Hkv;
+  if (p.G > 16) return hipErrorInvalidValue;
+  return a.D == 64 ? launch_d<64>(p, a.N, a.layout, stream) : launch_d<128>(p, a.N, a.layout, stream);
 }
 
 }  // namespace attn

@@ -92,7 +92,7 @@ def main():
 
     cd = CONFIGS["paged_decode_gqa"]
     wd = decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"], lmin=cd["lmin"],
-                       lmax=cd["lmax"], block_size=cd["block_size"])
+                       lmax=cd["lmax"], block_size=cd["block_size"], layout="mfma")
     dq = wd.q.to(dev)
     # two copies of the pool, used alternately, so that K/V cannot be served
     # from the 256 MB last-level cache of the previous step
@@ -109,7 +109,7 @@ def main():
 
     def run_decode(i):
         kp, vp = pools[i % 2]
-        A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws)
+        A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws, layout="mfma")
 
     # ------------------------------------------------------------ timed steps
     for i in range(args.warmup):
@@ -140,8 +140,8 @@ def main():
         "paged_decode_gqa": {
             "kv_GBps": round(dec_gbps, 1), "frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(dec_s * 1e6, 2), "us_min": round(min(t_dec) * 1e6, 2),
-            "kv_bytes": kv_bytes, "launches": "split + merge",
-            "traffic": measured_traffic("decode_split"),
+            "kv_bytes": kv_bytes, "launches": "split + merge", "pool_layout": "mfma",
+            "traffic": measured_traffic("decode_native"),
         },
     }
 
@@ -160,6 +160,23 @@ def main():
         return float(np.mean(ts)), float(np.min(ts))
 
     if not args.no_secondary:
+        # the same cache in the row-major pool layout (LDS-staged kernel)
+        wr = decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"],
+                           lmin=cd["lmin"], lmax=cd["lmax"], block_size=cd["block_size"])
+        rpools = [(wr.k_pool.to(dev), wr.v_pool.to(dev)) for _ in range(2)]
+        ctr = [0]
+
+        def run_rowmajor():
+            kp, vp = rpools[ctr[0] % 2]
+            ctr[0] += 1
+            A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws)
+        mr, nr = time_it(run_rowmajor, 20)
+        secondary["paged_decode_gqa_rowmajor_pools"] = {
+            "kv_GBps": round(kv_bytes / mr / 1e9, 1),
+            "frac_hbm_peak": round(kv_bytes / mr / 1e9 / PEAK_HBM_GBPS, 4),
+            "us_per_launch": round(mr * 1e6, 2), "us_min": round(nr * 1e6, 2)}
+        del rpools
+
         c3 = CONFIGS["gqa_causal_s8192"]
         w3 = prefill_inputs(c3["B"], c3["Hq"], c3["Hkv"], c3["S"], c3["D"], seed=c3["seed"])
         q3, k3, v3 = w3.q.to(dev), w3.k.to(dev), w3.v.to(dev)

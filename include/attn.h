@@ -15,7 +15,7 @@
  *   prefill  Q, O : [B, Hq,  S, D]     K, V : [B, Hkv, S, D]
  *            LSE  : float32 [B, Hq, S], natural logarithm
  *   decode   q, o : [N, Hq, D]         lse  : float32 [N, Hq]
- *            k_pool, v_pool : [num_blocks, Hkv, block_size, D]
+ *            k_pool, v_pool : see attn_kv_layout
  *            block_table    : int32 [N, max_blocks_per_seq]
  *            seq_lens       : int32 [N]
  *   bf16 tensors hold IEEE bfloat16 bit patterns (uint16_t).
@@ -37,6 +37,18 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Layouts of the paged K/V pools.  Both keep each (block, head) as one
+ * contiguous run of block_size * D elements; only the order inside the run
+ * differs.
+ *   ATTN_KV_ROWMAJOR: k_pool, v_pool [num_blocks, Hkv, block_size, D]
+ *   ATTN_KV_MFMA:     k_pool [num_blocks, Hkv, D/8, block_size, 8]  (8-element
+ *                     chunks of each token row, chunk-major)
+ *                     v_pool [num_blocks, Hkv, D, block_size]       (V transposed
+ *                     within the block)
+ * The MFMA layout lets every matrix-core operand be one coalesced load
+ * straight from HBM and is the faster one. */
+typedef enum { ATTN_KV_ROWMAJOR = 0, ATTN_KV_MFMA = 1 } attn_kv_layout;
 
 typedef enum {
   ATTN_OK = 0,
@@ -148,7 +160,8 @@ size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_blocks_p
  *
  *   q            : bf16 [N, Hq, D];  o : bf16 [N, Hq, D] (out)
  *   lse          : float32 [N, Hq] (out) or NULL
- *   k_pool/v_pool: bf16 [num_blocks, Hkv, block_size, D]
+ *   k_pool/v_pool: bf16 pools in the layout kv_layout names (attn_kv_layout)
+ *   kv_layout    : ATTN_KV_ROWMAJOR or ATTN_KV_MFMA
  *   block_table  : int32 [N, max_blocks_per_seq]; unused entries are ignored
  *   seq_lens     : int32 [N]
  *   block_size   : must be 16;  D in {64, 128};  Hq % Hkv == 0, Hq/Hkv <= 16
@@ -163,7 +176,7 @@ size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_blocks_p
  */
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                      void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
+                      int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
                       int num_blocks, int max_blocks_per_seq, float scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 

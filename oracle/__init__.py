@@ -13,4 +13,5 @@ from .attention import (  # noqa: F401
     ref_decode_paged,
     ref_blockskip,
     kv_head_of,
+    pool_rows,
 )

@@ -43,7 +43,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-__all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip"]
+__all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip", "pool_rows"]
 
 
 def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
@@ -107,18 +107,38 @@ def ref_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
     return out, lse
 
 
+def pool_rows(pool: np.ndarray, layout: str, which: str) -> np.ndarray:
+    """View a K or V pool as [NB, Hkv, block_size, D] (token rows).
+
+    "rowmajor" pools already are.  In the "mfma" layout each (block, head)
+    run stores K as 8-element chunks, chunk-major ([D/8, block_size, 8]),
+    and V transposed ([D, block_size]); only the order inside the run
+    differs, so this is a pure index permutation."""
+    if layout == "rowmajor":
+        return pool
+    if layout != "mfma":
+        raise ValueError(layout)
+    if which == "k":
+        NB, Hkv, nc, bs, eight = pool.shape
+        return pool.transpose(0, 1, 3, 2, 4).reshape(NB, Hkv, bs, nc * eight)
+    return pool.transpose(0, 1, 3, 2)
+
+
 def ref_decode_paged(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                      block_table: np.ndarray, seq_lens: np.ndarray,
-                     block_size: int, scale: float):
+                     block_size: int, scale: float, layout: str = "rowmajor"):
     """Decode attention over a paged KV cache [KV].
 
-    q: [N, Hq, D]; k_pool/v_pool: [NB, Hkv, block_size, D]; block_table:
-    [N, max_blocks] (entry j = physical block holding logical block j);
-    seq_lens: [N].  Cached token t of sequence n lives in physical block
-    block_table[n, t // block_size], slot t % block_size.  The new query sees
-    all L = seq_lens[n] cached tokens.  Returns (O [N, Hq, D], LSE [N, Hq]);
-    a sequence with L = 0 gets O = 0, LSE = -inf.
+    q: [N, Hq, D]; k_pool/v_pool: token rows [NB, Hkv, block_size, D] after
+    :func:`pool_rows`; block_table: [N, max_blocks] (entry j = physical block
+    holding logical block j); seq_lens: [N].  Cached token t of sequence n
+    lives in physical block block_table[n, t // block_size], slot
+    t % block_size.  The new query sees all L = seq_lens[n] cached tokens.
+    Returns (O [N, Hq, D], LSE [N, Hq]); a sequence with L = 0 gets O = 0,
+    LSE = -inf.
     """
+    k_pool = pool_rows(k_pool, layout, "k")
+    v_pool = pool_rows(v_pool, layout, "v")
     N, Hq, D = q.shape
     NB, Hkv, bs, Dk = k_pool.shape
     assert bs == block_size and Dk == D

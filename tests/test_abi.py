@@ -93,10 +93,11 @@ def test_decode_workspace_and_validation_without_device():
     need = A.attn_decode_workspace_bytes(2, 8, 128, 4, 16)
 
     def call(**kw):
-        a = dict(q=8, kp=8, vp=8, bt=8, sl=8, bs=16, o=8, N=2, Hq=8, Hkv=2, D=128, NB=8, MB=4,
-                 scale=0.1, ws=256, wsb=need)
+        a = dict(q=8, kp=8, vp=8, bt=8, sl=8, bs=16, lay=1, o=8, N=2, Hq=8, Hkv=2, D=128, NB=8,
+                 MB=4, scale=0.1, ws=256, wsb=need)
         a.update(kw)
-        return lib.attn_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["bs"], a["o"],
+        return lib.attn_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["bs"], a["lay"],
+                                     a["o"],
                                      None, a["N"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["MB"],
                                      a["scale"], a["ws"], a["wsb"], None)
     assert call(bt=None) == -1
@@ -105,6 +106,8 @@ def test_decode_workspace_and_validation_without_device():
     assert call(Hq=6, Hkv=4) == -1
     assert call(NB=0) == -1
     assert call(scale=float("inf")) == -1
+    assert call(lay=2) == -1
+    assert call(lay=-1) == -1
     assert call(bs=32) == -2
     assert call(D=80) == -2
     assert call(Hq=64, Hkv=2) == -2          # group of 32 query heads

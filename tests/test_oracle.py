@@ -333,3 +333,26 @@ def test_blockskip_qtile_subset_matches_full():
     rows = np.concatenate([np.arange(t * 16, (t + 1) * 16) for t in sel])
     np.testing.assert_array_equal(o[:, :, rows], o2)
     np.testing.assert_array_equal(s[:, :, sel], s2)
+
+
+def test_decode_layouts_hold_the_same_cache():
+    """The two pool layouts are index permutations of the same cache: the
+    generator draws identical values and the oracle gives identical results;
+    element checks pin both layout definitions."""
+    from oracle import pool_rows
+    a = decode_inputs(N=3, Hq=8, Hkv=2, D=16, seed=70, lmin=1, lmax=40, dtype="f32")
+    b = decode_inputs(N=3, Hq=8, Hkv=2, D=16, seed=70, lmin=1, lmax=40, dtype="f32", layout="mfma")
+    assert b.k_pool.shape == (a.num_blocks, 2, 2, 16, 8) and b.v_pool.shape == (a.num_blocks, 2, 16, 16)
+    ka, kb = a.k_pool.numpy(), b.k_pool.numpy()
+    va, vb = a.v_pool.numpy(), b.v_pool.numpy()
+    # K element (block p, head g, token t, dim d) sits at chunk d // 8, slot d % 8
+    assert kb[1, 1, 1, 5, 2] == ka[1, 1, 5, 8 + 2]
+    assert vb[2, 0, 7, 9] == va[2, 0, 9, 7]                 # V transposed in the block
+    np.testing.assert_array_equal(pool_rows(kb, "mfma", "k"), ka)
+    np.testing.assert_array_equal(pool_rows(vb, "mfma", "v"), va)
+    oa = ref_decode_paged(upcast_f64(a.q), upcast_f64(a.k_pool), upcast_f64(a.v_pool),
+                          a.block_table.numpy(), a.seq_lens.numpy(), 16, a.scale)
+    ob = ref_decode_paged(upcast_f64(b.q), upcast_f64(b.k_pool), upcast_f64(b.v_pool),
+                          b.block_table.numpy(), b.seq_lens.numpy(), 16, b.scale, layout="mfma")
+    np.testing.assert_array_equal(oa[0], ob[0])
+    np.testing.assert_array_equal(oa[1], ob[1])

@@ -117,7 +117,7 @@ def _run_decode(d, table=None, lens=None, k_pool=None, v_pool=None):
     vp = (d.v_pool if v_pool is None else v_pool).to(dev)
     bt = (d.block_table if table is None else table).to(dev)
     sl = (d.seq_lens if lens is None else lens).to(dev)
-    o, lse = A.decode_paged(q, kp, vp, bt, sl, d.block_size, d.scale)
+    o, lse = A.decode_paged(q, kp, vp, bt, sl, d.block_size, d.scale, layout=d.layout)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -126,22 +126,27 @@ def _ref_decode(d, table=None, lens=None):
     bt = (d.block_table if table is None else table).numpy()
     sl = (d.seq_lens if lens is None else lens).numpy()
     return ref_decode_paged(upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool), bt, sl,
-                            d.block_size, d.scale)
+                            d.block_size, d.scale, layout=d.layout)
 
 
-def test_paged_decode_full_config_nan_tails():
+LAYOUTS = ["rowmajor", "mfma"]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paged_decode_full_config_nan_tails(layout):
     c = CONFIGS["paged_decode_gqa"]
-    say("paged_decode_gqa full config, NaN-poisoned tail slots")
+    say(f"paged_decode_gqa full config, NaN-poisoned tail slots, {layout} pools")
     d = decode_inputs(c["N"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], lmin=c["lmin"],
-                      lmax=c["lmax"], tail="nan")
+                      lmax=c["lmax"], tail="nan", layout=layout)
     o, lse = _run_decode(d)
     ro, rl = _ref_decode(d)
     _compare(o, lse, ro, rl, TOL["bf16"], "decode c4")
 
 
-def test_paged_decode_permutation_bit_identical():
-    say("decode: physical block permutation leaves the output bit-identical")
-    d = decode_inputs(8, 32, 8, 128, seed=77, lmin=1, lmax=700)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paged_decode_permutation_bit_identical(layout):
+    say(f"decode: physical block permutation leaves the output bit-identical ({layout})")
+    d = decode_inputs(8, 32, 8, 128, seed=77, lmin=1, lmax=700, layout=layout)
     o1, l1 = _run_decode(d)
     perm = torch.from_numpy(np.random.default_rng(78).permutation(d.num_blocks))
     kp2 = torch.empty_like(d.k_pool); kp2[perm] = d.k_pool
@@ -157,10 +162,11 @@ def test_paged_decode_permutation_bit_identical():
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 128), (16, 1, 64), (8, 4, 64),
                                        (32, 2, 128)])
-def test_paged_decode_edge_lengths(Hq, Hkv, D):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paged_decode_edge_lengths(Hq, Hkv, D, layout):
     lens = [1, 15, 16, 17, 255, 256, 257, 1000, 0, 513]
-    say(f"decode edge lengths Hq{Hq} Hkv{Hkv} D{D} lens={lens}")
-    d = decode_inputs(len(lens), Hq, Hkv, D, seed=90 + D, lens=lens, tail="nan")
+    say(f"decode edge lengths Hq{Hq} Hkv{Hkv} D{D} {layout} lens={lens}")
+    d = decode_inputs(len(lens), Hq, Hkv, D, seed=90 + D, lens=lens, tail="nan", layout=layout)
     o, lse = _run_decode(d)
     ro, rl = _ref_decode(d)
     assert np.all(o[8] == 0) and np.all(np.isneginf(lse[8]))
@@ -168,9 +174,10 @@ def test_paged_decode_edge_lengths(Hq, Hkv, D):
     _compare(o[keep], lse[keep], ro[keep], rl[keep], TOL["bf16"], "decode edges")
 
 
-def test_paged_decode_bad_table_entries_give_nan():
-    say("decode: out-of-range table entry and too-long sequence -> NaN rows only")
-    d = decode_inputs(4, 8, 2, 128, seed=95, lens=[40, 40, 40, 40])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paged_decode_bad_table_entries_give_nan(layout):
+    say(f"decode: out-of-range table entry and too-long sequence -> NaN rows only ({layout})")
+    d = decode_inputs(4, 8, 2, 128, seed=95, lens=[40, 40, 40, 40], layout=layout)
     bt = d.block_table.clone()
     bt[1, 2] = d.num_blocks + 5          # out of range, inside the used blocks
     bt[2, 0] = -7

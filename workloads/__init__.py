@@ -21,8 +21,12 @@ table mapping logical to physical blocks).
 
 Layouts:
   * prefill Q/O: [B, Hq, S, D]; K/V: [B, Hkv, S, D] (contiguous, row-major)
-  * decode q/o: [N, Hq, D]; k_pool/v_pool: [NB, Hkv, block_size, D];
-    block_table: int32 [N, max_blocks_per_seq] (padding -1); seq_lens: int32 [N]
+  * decode q/o: [N, Hq, D]; block_table: int32 [N, max_blocks_per_seq]
+    (padding -1); seq_lens: int32 [N]; pools in one of two layouts, both with
+    one contiguous (block, head) run of block_size * D elements:
+      "rowmajor": k_pool, v_pool [NB, Hkv, block_size, D]
+      "mfma":     k_pool [NB, Hkv, D/8, block_size, 8]  (8-element chunks, chunk-major)
+                  v_pool [NB, Hkv, D, block_size]       (V transposed within the block)
 """
 from __future__ import annotations
 
@@ -99,6 +103,7 @@ class DecodeInputs:
     dtype: str
     seed: int
     perm: np.ndarray           # logical block id -> physical block id
+    layout: str = "rowmajor"
 
     @property
     def num_blocks(self) -> int:
@@ -164,7 +169,7 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
                   lmin: int = 512, lmax: int = 4096, block_size: int = 16,
                   tail: str = "zero", dtype: str = "bf16",
                   lens: Optional[list] = None,
-                  scale: Optional[float] = None) -> DecodeInputs:
+                  scale: Optional[float] = None, layout: str = "rowmajor") -> DecodeInputs:
     """Paged KV-cache decode inputs.
 
     Draw order: the N context lengths (uniform integers on [lmin, lmax],
@@ -175,6 +180,8 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
     physical block ``perm[base_n + j]``.  Unused slots of each sequence's last
     block hold zeros (``tail="zero"``) or NaN (``tail="nan"``, which a correct
     kernel never reads).  Padding entries of the block table are -1.
+    ``layout`` only rearranges elements inside each (block, head) run (see
+    the module docstring); the random draws are identical for both.
     """
     rng = np.random.default_rng(seed)
     if lens is None:
@@ -209,11 +216,19 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
         base += nblk[n]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if layout == "mfma":
+        if D % 8:
+            raise ValueError("the mfma layout needs D % 8 == 0")
+        kp = np.ascontiguousarray(
+            kp.reshape(NB, Hkv, block_size, D // 8, 8).transpose(0, 1, 3, 2, 4))
+        vp = np.ascontiguousarray(vp.transpose(0, 1, 3, 2))
+    elif layout != "rowmajor":
+        raise ValueError(layout)
     return DecodeInputs(
         q=to_dtype(q, dtype), k_pool=to_dtype(kp, dtype), v_pool=to_dtype(vp, dtype),
         block_table=torch.from_numpy(table), seq_lens=torch.from_numpy(lens_np.astype(np.int32)),
         block_size=block_size, N=N, Hq=Hq, Hkv=Hkv, D=D, max_blocks=max_blocks,
-        scale=float(scale), dtype=dtype, seed=seed, perm=perm)
+        scale=float(scale), dtype=dtype, seed=seed, perm=perm, layout=layout)
 
 
 # The five named workloads.  Sizes are the problem statement's; seeds are fixed
