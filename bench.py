@@ -7,8 +7,10 @@ prefill at the Llama-2-7B attention shape (B=4, Hq=Hkv=32, S=2048, D=128,
 bf16) followed by the paged GQA decode (64 sequences, lengths U[512,4096],
 Hq=32, Hkv=8, D=128, 16-token blocks).  Inputs are seeded synthetic tensors
 already resident in HBM.  W untimed warm-up steps, then exactly K timed steps
-bracketed by device synchronisations; each kernel is also timed with HIP
-events on the stream it is launched on.  Prints ONE JSON line.
+bracketed by device synchronisations: the K prefills back to back, then the
+K decodes, with HIP events before, between and after them on the stream the
+kernels run on, which gives each kernel's mean launch duration without
+per-launch marker gaps.  Prints ONE JSON line.
 
 `value` is the prefill throughput in TFLOP/s (algorithmic flops
 4*B*Hq*D*S(S+1)/2 over the prefill kernel's mean event time).  The decode
@@ -30,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-KERNEL_SOURCES = ["prefill_bf16.hip", "decode_paged.hip", "attn_api.cpp", "attn_internal.h"]
+GPU_SPIN_CYCLES = 4_000_000  # about 2 ms of GPU time before a timed region
 
 
 def kernel_hash(name: str) -> str:
@@ -62,6 +64,8 @@ def parse():
                     help="skip the GQA-8192 and block-skip measurements")
     ap.add_argument("--cpu-heads", type=int, default=128,
                     help="(batch, head) pairs of the prefill workload the CPU oracle runs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle sample until this much time has passed")
     return ap.parse_args()
 
 
@@ -85,8 +89,10 @@ def main():
     # ---------------------------------------------------------------- inputs
     cp = CONFIGS["mha_causal_s2048"]
     wp = prefill_inputs(cp["B"], cp["Hq"], cp["Hkv"], cp["S"], cp["D"], seed=cp["seed"])
-    q, k, v = wp.q.to(dev), wp.k.to(dev), wp.v.to(dev)
-    o = torch.empty_like(q)
+    # two copies of Q/K/V (2 x 192 MiB), used alternately, so that a launch
+    # cannot find its inputs in the 256 MB last-level cache
+    pre_in = [(wp.q.to(dev), wp.k.to(dev), wp.v.to(dev)) for _ in range(2)]
+    o = torch.empty_like(pre_in[0][0])
     lse = torch.empty((cp["B"], cp["Hq"], cp["S"]), dtype=torch.float32, device=dev)
     p_flops = prefill_flops(cp["B"], cp["Hq"], cp["S"], cp["D"], True)
 
@@ -94,8 +100,7 @@ def main():
     wd = decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"], lmin=cd["lmin"],
                        lmax=cd["lmax"], block_size=cd["block_size"], layout="mfma")
     dq = wd.q.to(dev)
-    # two copies of the pool, used alternately, so that K/V cannot be served
-    # from the 256 MB last-level cache of the previous step
+    # two copies of the pool (2 x 623 MB), used alternately, for the same reason
     pools = [(wd.k_pool.to(dev), wd.v_pool.to(dev)) for _ in range(2)]
     dbt, dsl = wd.block_table.to(dev), wd.seq_lens.to(dev)
     do = torch.empty_like(dq)
@@ -104,7 +109,8 @@ def main():
                      dtype=torch.uint8, device=dev)
     kv_bytes = wd.kv_bytes()
 
-    def run_prefill():
+    def run_prefill(i):
+        q, k, v = pre_in[i % 2]
         A.attn_prefill(q, k, v, o, lse, True, wp.scale)
 
     def run_decode(i):
@@ -112,52 +118,58 @@ def main():
         A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws, layout="mfma")
 
     # ------------------------------------------------------------ timed steps
+    # K steps = K prefills and K decodes.  The prefills are issued back to
+    # back, then the decodes, with one HIP event before, between and after,
+    # all on the stream the kernels are launched on (torch's current stream,
+    # passed through the C ABI).  A marker between every pair of launches
+    # would add an idle gap of about 10 us in front of each kernel.
     for i in range(args.warmup):
-        run_prefill()
+        run_prefill(i)
         run_decode(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # a short GPU-side spin ahead of the first event lets the host queue the
+    # launches before the timed region starts, so the first kernel does not
+    # wait for the host
+    torch.cuda._sleep(GPU_SPIN_CYCLES)
+    e0.record()
     for i in range(args.steps):
-        e = ev[i]
-        e[0].record()
-        run_prefill()
-        e[1].record()
-        e[2].record()
+        run_prefill(i)
+    e1.record()
+    for i in range(args.steps):
         run_decode(i)
-        e[3].record()
+    e2.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_pre = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
-    t_dec = [e[2].elapsed_time(e[3]) * 1e-3 for e in ev]
-    pre_s = float(np.mean(t_pre))
-    dec_s = float(np.mean(t_dec))
+    pre_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    dec_s = e1.elapsed_time(e2) * 1e-3 / args.steps
     pre_tflops = p_flops / pre_s / 1e12
     dec_gbps = kv_bytes / dec_s / 1e9
 
     secondary = {
         "paged_decode_gqa": {
             "kv_GBps": round(dec_gbps, 1), "frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
-            "us_per_launch": round(dec_s * 1e6, 2), "us_min": round(min(t_dec) * 1e6, 2),
-            "kv_bytes": kv_bytes, "launches": "split + merge", "pool_layout": "mfma",
+            "us_per_launch": round(dec_s * 1e6, 2),
+            "kv_bytes": kv_bytes, "launches": "decode_native + decode_merge", "pool_layout": "mfma",
             "traffic": measured_traffic("decode_native"),
         },
     }
 
     def time_it(fn, reps, warm=2):
+        """Mean time per launch of `reps` back-to-back launches (HIP events)."""
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
-        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for a, b in es:
-            a.record()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(GPU_SPIN_CYCLES)
+        a.record()
+        for _ in range(reps):
             fn()
-            b.record()
+        b.record()
         torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) * 1e-3 for a, b in es]
-        return float(np.mean(ts)), float(np.min(ts))
+        return a.elapsed_time(b) * 1e-3 / reps
 
     if not args.no_secondary:
         # the same cache in the row-major pool layout (LDS-staged kernel)
@@ -170,11 +182,11 @@ def main():
             kp, vp = rpools[ctr[0] % 2]
             ctr[0] += 1
             A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws)
-        mr, nr = time_it(run_rowmajor, 20)
+        mr = time_it(run_rowmajor, 20)
         secondary["paged_decode_gqa_rowmajor_pools"] = {
             "kv_GBps": round(kv_bytes / mr / 1e9, 1),
             "frac_hbm_peak": round(kv_bytes / mr / 1e9 / PEAK_HBM_GBPS, 4),
-            "us_per_launch": round(mr * 1e6, 2), "us_min": round(nr * 1e6, 2)}
+            "us_per_launch": round(mr * 1e6, 2)}
         del rpools
 
         c3 = CONFIGS["gqa_causal_s8192"]
@@ -182,7 +194,7 @@ def main():
         q3, k3, v3 = w3.q.to(dev), w3.k.to(dev), w3.v.to(dev)
         o3 = torch.empty_like(q3)
         l3 = torch.empty((1, c3["Hq"], c3["S"]), dtype=torch.float32, device=dev)
-        m3, n3 = time_it(lambda: A.attn_prefill(q3, k3, v3, o3, l3, True, w3.scale), 10)
+        m3 = time_it(lambda: A.attn_prefill(q3, k3, v3, o3, l3, True, w3.scale), 10)
         f3 = prefill_flops(1, c3["Hq"], c3["S"], c3["D"], True)
         secondary["gqa_causal_s8192"] = {
             "TFLOPs": round(f3 / m3 / 1e12, 1), "frac_mfma_peak": round(f3 / m3 / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -199,11 +211,11 @@ def main():
             o5 = torch.empty_like(q5)
             l5 = torch.empty((1, c5["Hq"], c5["S"]), dtype=torch.float32, device=dev)
             cnt = torch.zeros(1, dtype=torch.int64, device=dev)
-            m5, _ = time_it(lambda: A.attn_prefill_blockskip(q5, k5, v5, o5, l5, w5.scale,
+            m5 = time_it(lambda: A.attn_prefill_blockskip(q5, k5, v5, o5, l5, w5.scale,
                                                              c5["lam"], 64, None, cnt), 3, warm=1)
             cnt.zero_()
             A.attn_prefill_blockskip(q5, k5, v5, o5, l5, w5.scale, c5["lam"], 64, None, cnt)
-            md, _ = time_it(lambda: A.attn_prefill(q5, k5, v5, o5, l5, True, w5.scale), 3, warm=1)
+            md = time_it(lambda: A.attn_prefill(q5, k5, v5, o5, l5, True, w5.scale), 3, warm=1)
             torch.cuda.synchronize()
             nT = c5["S"] // 64
             live = c5["Hq"] * nT * (nT + 1) // 2
@@ -230,10 +242,15 @@ def main():
         qs = upcast_f64(wp.q[:1, :nh])
         ks = upcast_f64(wp.k[:1, :nh])
         vs = upcast_f64(wp.v[:1, :nh])
-        t1 = time.perf_counter()
-        ref_prefill(qs, ks, vs, causal=True, scale=wp.scale)
-        tc = time.perf_counter() - t1
-        fl = prefill_flops(1, nh, cp["S"], cp["D"], True)
+        # repeat the sample until about --cpu-seconds of CPU work has been timed
+        reps, t1 = 0, time.perf_counter()
+        while True:
+            ref_prefill(qs, ks, vs, causal=True, scale=wp.scale)
+            reps += 1
+            tc = time.perf_counter() - t1
+            if tc >= args.cpu_seconds:
+                break
+        fl = prefill_flops(1, nh, cp["S"], cp["D"], True) * reps
         try:
             from threadpoolctl import threadpool_info
             cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
@@ -242,7 +259,8 @@ def main():
         cpu = {"value": round(fl / tc / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
                "kind": "oracle",
                "sample": f"fp64 numpy oracle, {nh} of {cp['B'] * cp['Hq']} (batch, head) pairs of "
-                         f"the S=2048 D=128 causal prefill, all rows; {tc:.2f} s"}
+                         f"the S=2048 D=128 causal prefill, all rows, run {reps} times; "
+                         f"{tc:.2f} s"}
 
     traffic = measured_traffic("prefill_bf16")
     out = {
@@ -252,7 +270,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round((pre_s + dec_s) * 1e3, 4),
+        "wall_s_timed_region": round(wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -265,8 +284,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "prefill_bf16_kernel<128,causal>",
-                     "us_per_launch": round(pre_s * 1e6, 2), "us_min": round(min(t_pre) * 1e6, 2),
-                     "flops_per_launch": p_flops},
+                     "us_per_launch": round(pre_s * 1e6, 2), "flops_per_launch": p_flops,
+                     "timing": f"HIP events around {args.steps} back-to-back launches"},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
