@@ -46,7 +46,7 @@ struct DecodeArgs {
 };
 
 // Tokens handled by one split-KV workgroup of the decode kernel.
-constexpr int kDecodeSplitTokens = 256;
+constexpr int kDecodeSplitTokens = 512;
 
 inline int decode_num_splits(int max_blocks, int block_size) {
   long long tokens = (long long)max_blocks * block_size;

@@ -13,21 +13,27 @@
 // Design (CDNA4, wave64):
 //  * A workgroup is 8 waves.  It owns one K/V head and `gw` of its query
 //    heads (gw = largest of 8,4,2,1 dividing Hq/Hkv) over 32*8/gw query rows;
-//    every wave owns 32 query rows of one head.  Each 64-key K/V tile is read
-//    from HBM/L2 once per workgroup, staged in LDS and used by all 8 waves.
+//    every wave owns 32 query rows of one head.  Each 64-key K/V tile is
+//    copied HBM/L2 -> LDS once per workgroup (global_load_lds_dwordx4, no
+//    register round trip) into a 4-stage ring and read by all 8 waves.
+//    LDS rows are padded (K 16 bytes, V 64 bytes per row) so that every
+//    operand read below is bank-conflict free with compile-time offsets.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims read
 //    from LDS, B = the wave's Q fragment held in VGPRs for the whole loop.
 //    In the 32x32 accumulator each lane holds one query (column) and 16 of
 //    the 32 keys, so a row maximum is an in-lane max plus one exchange with
-//    lane ^ 32, and the running max/sum rescale is a per-lane scalar.
-//  * O^T += V^T P^T with the same instruction: A = 32 dims x 16 keys of V^T
-//    from LDS, B = P^T taken straight from the score accumulator (rounded to
-//    bf16).  The reduction (k) order of an MFMA is free as long as both
-//    operands agree, so V is written to LDS transposed, with the 4-key
-//    chunks of each 16-key group placed in the order the accumulator hands
-//    out keys; each A fragment is then one 16-byte LDS read.
-//  * Softmax runs in base 2: scores are scaled by scale*log2(e) inside one
-//    FMA and exponentiated with v_exp_f32.
+//    lane ^ 32 (v_permlane32_swap), and the running max/sum are per-lane.
+//  * O^T += V^T P^T with the same instruction: B = P^T straight from the
+//    score accumulator rounded to bf16, A = V^T fragments from the
+//    transposing LDS read (ds_read_b64_tr_b16).  The reduction order of an
+//    MFMA is free as long as both operands agree, so keys are taken in the
+//    order the accumulator hands them out.
+//  * Softmax runs in base 2 (scale * log2(e) folded into one FMA, v_exp_f32)
+//    with a lazy rescale; row sums use v_dot2 on the bf16-rounded P.
+//  * Ping-pong: the two waves of a SIMD alternate a pure-MFMA phase and a
+//    pure-VALU (softmax) phase, half an iteration apart, so the matrix core
+//    and the vector ALU work at the same time (a single wave that mixes
+//    both does not overlap them on this hardware).
 //  * Causal: key tiles past a wave's last row are skipped per wave; only
 //    diagonal tiles are masked.  Heavy query blocks are scheduled first.
 #include "attn_internal.h"
@@ -158,10 +164,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   const int sub = hg % p.sub_per_kv;
   const int bk = hg / p.sub_per_kv;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
-  const int head = kvh * p.G + sub * p.gw + (wave % p.gw);
+  // Waves w and w+4 share a SIMD.  Without block skip they run the tile
+  // loop half an iteration apart (see below), so they get adjacent 32-row
+  // slots: equal causal tile counts keep both busy to the end.
+  const int slot = SKIP ? wave : ((wave & 3) << 1) | (wave >> 2);
+  const int head = kvh * p.G + sub * p.gw + (slot % p.gw);
   const int S = p.S;
   const int row0 = qblk * p.rows_per_wg;
-  const int q0 = row0 + (wave / p.gw) * 32;
+  const int q0 = row0 + (slot / p.gw) * 32;
 
   const int wg_last = min(S, row0 + p.rows_per_wg) - 1;
   const int n_tiles = CAUSAL ? wg_last / BN + 1 : (S + BN - 1) / BN;
@@ -303,10 +313,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     }
     return half_swap_max(fmaxf(m0, m1)) * sl2;
   };
-  // softmax of a score tile and O^T += V^T P^T for key tile t.  The
+  // softmax of a score tile into bf16 P (packed for the P.V MFMA).  The
   // exponent reference moves (with a rescale of O and l) only when the row
   // max grew by more than 8, a factor 256; the result is exact after 1/l.
-  auto finish = [&](int t, f32x16* sc, float tmx) {
+  auto softmax = [&](f32x16* sc, float tmx, uint32_t (*pk)[8]) {
     if (__any(tmx > m_used + 8.f)) {
       const float m_new = fmaxf(m_used, tmx);
       const float alpha = fast_exp2(m_used - m_new);
@@ -318,7 +328,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
       m_used = m_new;
     }
     const float nm = -m_used;
-    uint32_t pk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -333,6 +342,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
       rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[1][j]), kOnes2, rs1, false);
     }
     l += rs0 + rs1;
+  };
+  // O^T += V^T P^T for key tile t; V^T fragments come from the transposing
+  // LDS read, running ahead of the MFMAs
+  auto pv = [&](int t, uint32_t (*pk)[8]) {
     const LDS_AS unsigned char* vl = smem + (t % T::NST) * T::STAGE + T::KT + v_base;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -351,6 +364,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
         }
       }
+    // three MFMAs' operands ahead, then alternate one MFMA / two reads
+    constexpr int NM = 4 * NDB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < NM - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  };
+  auto finish = [&](int t, f32x16* sc, float tmx) {
+    uint32_t pk[2][8];
+    softmax(sc, tmx, pk);
+    pv(t, pk);
   };
   // block-skip vote of this wave's 32 rows for key tile t, published in LDS
   auto publish_vote = [&](int t, float tmx_t) {
@@ -373,42 +400,68 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     return sk;
   };
 
-  // The two waves sharing a SIMD (w and w+4) run the tile loop out of phase
-  // so that one's softmax VALU work overlaps the other's MFMAs: role A does
-  // Q.K^T, softmax and P.V of tile t; role B finishes tile t-1 (softmax,
-  // P.V) and then computes Q.K^T of tile t.  The block-skip decision needs
-  // both halves of a 64-row tile first, so with block skip every wave is B.
-  const bool role_b = SKIP || ((wave >> 2) & 1);
   f32x16 sc[2];
-  float tmx_prev = -INFINITY;
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
+  if constexpr (!SKIP) {
+    // Ping-pong.  Each wave alternates an MFMA phase (P.V of tile j-1, then
+    // Q.K^T of tile j) and a VALU phase (mask, row max and softmax of tile
+    // j), separated by workgroup barriers.  The second wave of each SIMD
+    // (waves 4-7, group 1) runs one barrier behind the first, so at every
+    // moment one wave of the pair feeds the matrix core while the other's
+    // exponentials run on the vector ALU; a wave that mixed both kinds of
+    // work in one stream would not overlap them.  Both groups run the same
+    // code, so the scores and P never need registers at the same time.
+    //
+    // DMA: group 0 issues its share of tile j+2 in its VALU phase j, group
+    // 1 its share of tile j+3 (and of tile 2 in its extra first slot); the
+    // issue stalls the issuing wave, and an MFMA-phase wave would hold the
+    // matrix core idle meanwhile.  The stage a share overwrites was last
+    // read before the preceding barrier.  Before the barrier that precedes
+    // the first Q.K^T of tile j+1, every wave waits until only its newest
+    // share (tile j+2) is in flight.
+    const int grp = wave >> 2;
+    uint32_t pk[2][8];
+    auto wait_tail = [&](int j) {
+      if (j + 2 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
+    };
+    if (n_tiles > 1) wait_all_but_newest(); else wait_vmem<0>();
     block_barrier();
-    if (t + 2 < n_tiles) issue(t + 2);
-    // role B: finish tile t-1
-    if (role_b && t >= 1 && t - 1 < wave_tiles) {
-      bool sk = false;
-      if constexpr (SKIP) sk = decide(t - 1);
-      if (!sk) finish(t - 1, sc, tmx_prev);
-      m_true = fmaxf(m_true, tmx_prev);
+    if (grp == 1) {
+      if (2 < n_tiles) issue(2);
+      block_barrier();
     }
-    // both roles: scores of tile t
-    if (t < wave_tiles) {
-      qk(t, sc);
-      tmx_prev = row_max(t, sc);
+    for (int j = 0; j <= n_tiles; ++j) {
+      if (j >= 1 && j - 1 < wave_tiles) pv(j - 1, pk);
+      if (j < wave_tiles) qk(j, sc);
+      if (grp == 1) wait_tail(j);
+      block_barrier();
+      if (j + 2 + grp < n_tiles) issue(j + 2 + grp);
+      if (j < wave_tiles) softmax(sc, row_max(j, sc), pk);
+      if (grp == 0) wait_tail(j);
+      block_barrier();
     }
-    // role A: finish tile t
-    if (!role_b && t < wave_tiles) finish(t, sc, tmx_prev);
-    if constexpr (SKIP) publish_vote(t, tmx_prev);
-  }
-  if (role_b) {
-    if constexpr (SKIP) block_barrier();
+    if (grp == 0) block_barrier();
+  } else {
+    // Block skip: the decision on a 64-row tile needs the row maxima of both
+    // of its waves, published in LDS, so every wave scores tile t, votes,
+    // and finishes tile t-1 after the next barrier.
+    float tmx_prev = -INFINITY;
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
+      block_barrier();
+      if (t + 2 < n_tiles) issue(t + 2);
+      if (t >= 1 && t - 1 < wave_tiles) {
+        if (!decide(t - 1)) finish(t - 1, sc, tmx_prev);
+        m_true = fmaxf(m_true, tmx_prev);
+      }
+      if (t < wave_tiles) {
+        qk(t, sc);
+        tmx_prev = row_max(t, sc);
+      }
+      publish_vote(t, tmx_prev);
+    }
+    block_barrier();
     const int t = n_tiles - 1;
-    if (t < wave_tiles) {
-      bool sk = false;
-      if constexpr (SKIP) sk = decide(t);
-      if (!sk) finish(t, sc, tmx_prev);
-    }
+    if (t < wave_tiles && !decide(t)) finish(t, sc, tmx_prev);
   }
 
   if (SKIP && lane == 0 && skipped && p.skip_count)

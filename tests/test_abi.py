@@ -87,8 +87,9 @@ def test_blockskip_validation_without_device():
 
 def test_decode_workspace_and_validation_without_device():
     lib = A.load()
-    # 64 sequences, 32 query heads, D=128, 256 blocks of 16 tokens -> 16 splits of 256 tokens
-    assert A.attn_decode_workspace_bytes(64, 32, 128, 256, 16) == 64 * 32 * 16 * 129 * 4
+    # 64 sequences, 32 query heads, D=128, 256 blocks of 16 tokens -> 8 splits of 512 tokens
+    assert A.attn_decode_workspace_bytes(64, 32, 128, 256, 16) == 64 * 32 * 8 * 129 * 4
+    assert A.attn_decode_workspace_bytes(1, 1, 64, 33, 16) == 1 * 1 * 2 * 65 * 4
     assert A.attn_decode_workspace_bytes(0, 32, 128, 256, 16) == 0
     need = A.attn_decode_workspace_bytes(2, 8, 128, 4, 16)
 

@@ -164,12 +164,13 @@ def test_paged_decode_permutation_bit_identical(layout):
                                        (32, 2, 128)])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_paged_decode_edge_lengths(Hq, Hkv, D, layout):
-    lens = [1, 15, 16, 17, 255, 256, 257, 1000, 0, 513]
+    lens = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000, 0, 1024, 1025, 1537]
     say(f"decode edge lengths Hq{Hq} Hkv{Hkv} D{D} {layout} lens={lens}")
     d = decode_inputs(len(lens), Hq, Hkv, D, seed=90 + D, lens=lens, tail="nan", layout=layout)
     o, lse = _run_decode(d)
     ro, rl = _ref_decode(d)
-    assert np.all(o[8] == 0) and np.all(np.isneginf(lse[8]))
+    z = lens.index(0)
+    assert np.all(o[z] == 0) and np.all(np.isneginf(lse[z]))
     keep = [i for i in range(len(lens)) if lens[i] > 0]
     _compare(o[keep], lse[keep], ro[keep], rl[keep], TOL["bf16"], "decode edges")
 
