@@ -247,12 +247,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
-  // Complete the Q loads with a wait the compiler can see (vmcnt(0)), so it
+  // The first two tile copies go out together with the Q loads; then one
+  // wait the compiler can see (vmcnt(0)) completes all of them, so it
   // places no vector-memory waits of its own inside the loop, where they
   // would also drain the tile prefetches.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
   issue(0);
   if (n_tiles > 1) issue(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // per-lane LDS offsets of the MFMA operand reads (see Tile)
   const int k_base = n * T::RK + hf * 16;                 // + kb*32*RK + ks*32
