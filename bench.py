@@ -80,7 +80,8 @@ def main():
     import torch
 
     import attention_flash_attn_fwd_amd as A
-    from workloads import CONFIGS, blockskip_inputs, decode_inputs, prefill_flops, prefill_inputs
+    from workloads import (CONFIGS, blockskip_inputs, decode_inputs, prefill_flops, prefill_inputs,
+                           shared_prefix_decode_inputs)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -188,6 +189,33 @@ def main():
             "frac_hbm_peak": round(kv_bytes / mr / 1e9 / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(mr * 1e6, 2)}
         del rpools
+
+        # shared prompts (copy-on-write block tables): 16 prompts of 1536
+        # tokens, 4 samples each with U[1, 2048] own tokens; the kernel reads
+        # every sequence's logical K/V, shared blocks once per sequence
+        ds, _ = shared_prefix_decode_inputs(16, 4, cd["Hq"], cd["Hkv"], cd["D"], seed=2004,
+                                            prefix_len=1536, suffix_min=1, suffix_max=2048,
+                                            layout="mfma")
+        sq, sbt, ssl = ds.q.to(dev), ds.block_table.to(dev), ds.seq_lens.to(dev)
+        spools = [(ds.k_pool.to(dev), ds.v_pool.to(dev)) for _ in range(2)]
+        sws = torch.empty(A.attn_decode_workspace_bytes(ds.N, cd["Hq"], cd["D"], ds.max_blocks, 16),
+                          dtype=torch.uint8, device=dev)
+        so = torch.empty_like(sq)
+        slse = torch.empty((ds.N, cd["Hq"]), dtype=torch.float32, device=dev)
+        sctr = [0]
+
+        def run_shared():
+            kp, vp = spools[sctr[0] % 2]
+            sctr[0] += 1
+            A.attn_decode_paged(sq, kp, vp, sbt, ssl, 16, so, slse, ds.scale, sws, layout="mfma")
+        ms = time_it(run_shared, 20)
+        logical = ds.kv_bytes()
+        unique = ds.num_blocks * cd["Hkv"] * 16 * cd["D"] * 2 * 2
+        secondary["paged_decode_shared_prefix"] = {
+            "logical_kv_GBps": round(logical / ms / 1e9, 1), "us_per_launch": round(ms * 1e6, 2),
+            "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "note": "16 prompts x 4 samples, 1536-token shared prompt, U[1,2048] own tokens"}
+        del spools
 
         c3 = CONFIGS["gqa_causal_s8192"]
         w3 = prefill_inputs(c3["B"], c3["Hq"], c3["Hkv"], c3["S"], c3["D"], seed=c3["seed"])

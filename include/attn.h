@@ -162,7 +162,11 @@ size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_blocks_p
  *   lse          : float32 [N, Hq] (out) or NULL
  *   k_pool/v_pool: bf16 pools in the layout kv_layout names (attn_kv_layout)
  *   kv_layout    : ATTN_KV_ROWMAJOR or ATTN_KV_MFMA
- *   block_table  : int32 [N, max_blocks_per_seq]; unused entries are ignored
+ *   block_table  : int32 [N, max_blocks_per_seq]; unused entries are ignored.
+ *                  Entries of different sequences may name the same physical
+ *                  block (prompt blocks shared copy-on-write between the
+ *                  samples of one prompt, same page, PageAttention part): the
+ *                  pools are only read.
  *   seq_lens     : int32 [N]
  *   block_size   : must be 16;  D in {64, 128};  Hq % Hkv == 0, Hq/Hkv <= 16
  *   workspace    : device buffer of at least

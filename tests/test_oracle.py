@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from oracle import ref_prefill, ref_decode_paged, ref_blockskip, kv_head_of
-from workloads import decode_inputs, upcast_f64
+from workloads import (decode_inputs, shared_prefix_decode_inputs, to_dtype, unshared_copy,
+                       upcast_f64)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -246,6 +247,45 @@ def test_decode_empty_sequence():
                               d.block_table.numpy(), d.seq_lens.numpy(), 16, d.scale)
     assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
     assert np.isfinite(o[1:]).all()
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "mfma"])
+def test_shared_prefix_cache(layout):
+    """Copy-on-write sharing (PageAttention part of the KV-cache survey page):
+    the samples of a prompt alias the prompt's full blocks, own a copy of its
+    partly filled last block, and read exactly the logical sequence they
+    would read from an unshared cache."""
+    P, M, Lp = 3, 4, 37
+    d, logical = shared_prefix_decode_inputs(P, M, 8, 2, 16, seed=53, prefix_len=Lp,
+                                             suffix_min=1, suffix_max=40, dtype="f32",
+                                             tail="nan", layout=layout)
+    bt = d.block_table.numpy()
+    ns = Lp // 16
+    for p_ in range(P):
+        rows = bt[p_ * M:(p_ + 1) * M]
+        assert (rows[:, :ns] == rows[0, :ns]).all()             # aliased prompt blocks
+        assert len(set(rows[:, ns].tolist())) == M              # one private copy each
+    private = [int(x) for n in range(d.N) for x in bt[n, ns:] if x >= 0]
+    assert len(private) == len(set(private))
+    assert d.num_blocks < unshared_copy(d).num_blocks
+    args = (upcast_f64(d.q),)
+    o, lse = ref_decode_paged(*args, upcast_f64(d.k_pool), upcast_f64(d.v_pool), bt,
+                              d.seq_lens.numpy(), 16, d.scale, layout=layout)
+    u = unshared_copy(d)
+    o2, lse2 = ref_decode_paged(*args, upcast_f64(u.k_pool), upcast_f64(u.v_pool),
+                                u.block_table.numpy(), u.seq_lens.numpy(), 16, d.scale,
+                                layout=layout)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    # each sequence: the last causal row of a prefill over its logical K/V
+    for n in range(d.N):
+        K, V = (upcast_f64(to_dtype(x, "f32")) for x in logical[n])
+        L = K.shape[0]
+        qq = np.zeros((1, d.Hq, L, d.D)); qq[0, :, L - 1] = args[0][n]
+        op, lp = ref_prefill(qq, K.transpose(1, 0, 2)[None], V.transpose(1, 0, 2)[None],
+                             causal=True, scale=d.scale, rows=[L - 1])
+        np.testing.assert_allclose(o[n], op[0, :, 0], atol=1e-13)
+        np.testing.assert_allclose(lse[n], lp[0, :, 0], atol=1e-13)
 
 
 # -------------------------------------------------------------------- blockskip

@@ -16,7 +16,8 @@ import torch
 
 import attention_flash_attn_fwd_amd as A
 from oracle import ref_blockskip, ref_decode_paged, ref_prefill
-from workloads import CONFIGS, blockskip_inputs, decode_inputs, prefill_inputs, upcast_f64
+from workloads import (CONFIGS, blockskip_inputs, decode_inputs, prefill_inputs,
+                       shared_prefix_decode_inputs, unshared_copy, upcast_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +190,19 @@ def test_paged_decode_bad_table_entries_give_nan(layout):
     assert np.isnan(o[2]).all() and np.isnan(o[3]).all()
     ro, rl = _ref_decode(d)
     _compare(o[:1], lse[:1], ro[:1], rl[:1], TOL["bf16"], "decode good row")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paged_decode_shared_prefix(layout):
+    say(f"decode: 8 prompts x 8 samples sharing 1000-token prompts (copy-on-write), {layout}")
+    d, _ = shared_prefix_decode_inputs(8, 8, 32, 8, 128, seed=96, prefix_len=1000,
+                                       suffix_min=1, suffix_max=600, tail="nan", layout=layout)
+    o, lse = _run_decode(d)
+    ro, rl = _ref_decode(d)
+    _compare(o, lse, ro, rl, TOL["bf16"], "decode shared prefix")
+    # the same logical cache without sharing gives the identical bits
+    o2, l2 = _run_decode(unshared_copy(d))
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
 
 
 # ---------------------------------------------------------------- block skip

@@ -39,7 +39,8 @@ import torch
 
 __all__ = [
     "PrefillInputs", "DecodeInputs", "CONFIGS",
-    "prefill_inputs", "blockskip_inputs", "decode_inputs", "to_dtype",
+    "prefill_inputs", "blockskip_inputs", "decode_inputs", "shared_prefix_decode_inputs",
+    "unshared_copy", "to_dtype",
     "upcast_f64", "prefill_flops",
 ]
 
@@ -216,19 +217,121 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
         base += nblk[n]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if layout == "mfma":
-        if D % 8:
-            raise ValueError("the mfma layout needs D % 8 == 0")
-        kp = np.ascontiguousarray(
-            kp.reshape(NB, Hkv, block_size, D // 8, 8).transpose(0, 1, 3, 2, 4))
-        vp = np.ascontiguousarray(vp.transpose(0, 1, 3, 2))
-    elif layout != "rowmajor":
-        raise ValueError(layout)
+    kp, vp = _to_layout(kp, vp, layout, block_size, D)
     return DecodeInputs(
         q=to_dtype(q, dtype), k_pool=to_dtype(kp, dtype), v_pool=to_dtype(vp, dtype),
         block_table=torch.from_numpy(table), seq_lens=torch.from_numpy(lens_np.astype(np.int32)),
         block_size=block_size, N=N, Hq=Hq, Hkv=Hkv, D=D, max_blocks=max_blocks,
         scale=float(scale), dtype=dtype, seed=seed, perm=perm, layout=layout)
+
+
+def shared_prefix_decode_inputs(n_prompts: int, n_samples: int, Hq: int, Hkv: int, D: int, *,
+                                seed: int, prefix_len: int, suffix_min: int, suffix_max: int,
+                                block_size: int = 16, tail: str = "zero", dtype: str = "bf16",
+                                scale: Optional[float] = None, layout: str = "rowmajor"):
+    """Decode inputs whose sequences share prompt blocks (copy-on-write).
+
+    Per the PageAttention part of the "LLM推理优化技术综述" page, several
+    outputs generated from one prompt share the prompt's K/V blocks, and a
+    block is copied only when it is written to.  Sequence n = p * n_samples
+    + m (sample m of prompt p) holds the prompt's prefix_len tokens followed
+    by its own suffix.  The prompt's full blocks (prefix_len // block_size of
+    them) are physical blocks referenced by all its samples' table rows; the
+    partly filled last prompt block is copied into each sample, which then
+    appends its own tokens there.
+
+    Draw order: the N suffix lengths (uniform integers on [suffix_min,
+    suffix_max]), q [N,Hq,D], per prompt its prefix K then V
+    ([prefix_len,Hkv,D]), per sequence its suffix K then V, then one
+    permutation of the physical blocks (shared blocks numbered first, prompt
+    by prompt, then each sequence's private blocks).
+
+    Returns (DecodeInputs, logical) where logical[n] = (K, V) float32 arrays
+    [L, Hkv, D] of sequence n before the dtype rounding.
+    """
+    rng = np.random.default_rng(seed)
+    bs = block_size
+    N = n_prompts * n_samples
+    suffix = rng.integers(suffix_min, suffix_max, size=N, endpoint=True).astype(np.int64)
+    lens = prefix_len + suffix
+    q = rng.standard_normal((N, Hq, D), dtype=np.float32)
+    pre = []
+    for _ in range(n_prompts):
+        pk = rng.standard_normal((prefix_len, Hkv, D), dtype=np.float32)
+        pv = rng.standard_normal((prefix_len, Hkv, D), dtype=np.float32)
+        pre.append((pk, pv))
+    logical = []
+    for n in range(N):
+        sk = rng.standard_normal((int(suffix[n]), Hkv, D), dtype=np.float32)
+        sv = rng.standard_normal((int(suffix[n]), Hkv, D), dtype=np.float32)
+        pk, pv = pre[n // n_samples]
+        logical.append((np.concatenate([pk, sk]), np.concatenate([pv, sv])))
+    n_shared = prefix_len // bs
+    nblk = [(int(L) + bs - 1) // bs for L in lens]
+    NB = n_prompts * n_shared + sum(nb - n_shared for nb in nblk)
+    max_blocks = max(nblk)
+    perm = rng.permutation(NB)
+    fill = np.nan if tail == "nan" else 0.0
+    kp = np.full((NB, Hkv, bs, D), fill, dtype=np.float32)
+    vp = np.full((NB, Hkv, bs, D), fill, dtype=np.float32)
+    table = np.full((N, max_blocks), -1, dtype=np.int32)
+
+    def put(phys, K, V, t0, t1):
+        kp[phys, :, : t1 - t0, :] = K[t0:t1].transpose(1, 0, 2)
+        vp[phys, :, : t1 - t0, :] = V[t0:t1].transpose(1, 0, 2)
+
+    for p in range(n_prompts):
+        for j in range(n_shared):
+            phys = int(perm[p * n_shared + j])
+            put(phys, pre[p][0], pre[p][1], j * bs, (j + 1) * bs)
+            for m in range(n_samples):
+                table[p * n_samples + m, j] = phys
+    nxt = n_prompts * n_shared
+    for n in range(N):
+        K, V = logical[n]
+        L = int(lens[n])
+        for j in range(n_shared, nblk[n]):
+            phys = int(perm[nxt])
+            nxt += 1
+            put(phys, K, V, j * bs, min(L, (j + 1) * bs))
+            table[n, j] = phys
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kp, vp = _to_layout(kp, vp, layout, bs, D)
+    d = DecodeInputs(
+        q=to_dtype(q, dtype), k_pool=to_dtype(kp, dtype), v_pool=to_dtype(vp, dtype),
+        block_table=torch.from_numpy(table), seq_lens=torch.from_numpy(lens.astype(np.int32)),
+        block_size=bs, N=N, Hq=Hq, Hkv=Hkv, D=D, max_blocks=max_blocks,
+        scale=float(scale), dtype=dtype, seed=seed, perm=perm, layout=layout)
+    return d, logical
+
+
+def unshared_copy(d: DecodeInputs) -> DecodeInputs:
+    """The same cache with every table entry pointing at a private copy of
+    its block (data movement only: blocks are copied whole, in order)."""
+    table = d.block_table.numpy()
+    N, MB = table.shape
+    used = [(n, j) for n in range(N) for j in range(MB) if table[n, j] >= 0]
+    src = torch.tensor([int(table[n, j]) for n, j in used], dtype=torch.long)
+    new_table = np.full_like(table, -1)
+    for i, (n, j) in enumerate(used):
+        new_table[n, j] = i
+    return dataclasses.replace(d, k_pool=d.k_pool[src].clone(), v_pool=d.v_pool[src].clone(),
+                               block_table=torch.from_numpy(new_table),
+                               perm=np.arange(len(used)))
+
+
+def _to_layout(kp: np.ndarray, vp: np.ndarray, layout: str, bs: int, D: int):
+    """Rearrange row-major pools [NB, Hkv, bs, D] into ``layout``."""
+    if layout == "mfma":
+        if D % 8:
+            raise ValueError("the mfma layout needs D % 8 == 0")
+        NB, Hkv = kp.shape[:2]
+        kp = np.ascontiguousarray(kp.reshape(NB, Hkv, bs, D // 8, 8).transpose(0, 1, 3, 2, 4))
+        vp = np.ascontiguousarray(vp.transpose(0, 1, 3, 2))
+    elif layout != "rowmajor":
+        raise ValueError(layout)
+    return kp, vp
 
 
 # The five named workloads.  Sizes are the problem statement's; seeds are fixed
