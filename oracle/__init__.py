@@ -14,4 +14,5 @@ from .attention import (  # noqa: F401
     ref_blockskip,
     kv_head_of,
     pool_rows,
+    ref_decode_paged_blockskip,
 )

@@ -43,7 +43,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-__all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip", "pool_rows"]
+__all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip", "pool_rows",
+           "ref_decode_paged_blockskip"]
 
 
 def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
@@ -230,4 +231,78 @@ def ref_blockskip(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
                 out[b, h, r_out:r_out + len(ri)] = p @ vg
                 lse[b, h, r_out:r_out + len(ri)] = l
                 r_out += len(ri)
+    return out, lse, skip, gap
+
+
+def ref_decode_paged_blockskip(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                               block_table: np.ndarray, seq_lens: np.ndarray,
+                               block_size: int, scale: float, *, lam: float,
+                               split_tokens: int, layout: str = "rowmajor"):
+    """Paged decode [KV] with BLASST block skipping [BLASST] inside each split.
+
+    The cached tokens of sequence n are cut into splits of ``split_tokens``
+    (a multiple of block_size) processed independently, as a split-KV
+    decode does; inside a split the pool blocks are walked in ascending
+    order.  For K/V head g and block b of a split, every query head h of the
+    group has the block maximum tm_h (scaled scores of the block's cached
+    tokens) and the running maximum m_h over the split's earlier blocks.  The
+    block is skipped when, for every h, m_h > -inf and tm_h - m_h < ln(lam):
+    its V load, exp and P.V are left out, for the whole group at once (the V
+    block is shared).  The first block of a split is never skipped.  A
+    skipped block has tm_h < m_h for every h, so folding it into the maximum
+    changes nothing and m_h is the plain prefix maximum over the split's
+    earlier blocks, which is what is evaluated here.
+
+    Returns (O [N,Hq,D], LSE [N,Hq], skip [N,Hkv,max_blocks] bool,
+    gap [N,Hkv,max_blocks]) with O/LSE the attention over the kept blocks'
+    tokens, gap = max_h (tm_h - m_h) (+inf at a split's first block, -inf
+    for unused blocks); skip <=> gap < ln(lam).
+    """
+    if not (0.0 < lam < 1.0):
+        raise ValueError("lambda must lie in (0, 1)")
+    if split_tokens % block_size:
+        raise ValueError("split_tokens must be a multiple of block_size")
+    k_pool = pool_rows(k_pool, layout, "k")
+    v_pool = pool_rows(v_pool, layout, "v")
+    N, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_pool.shape
+    G = Hq // Hkv
+    MB = block_table.shape[1]
+    bps = split_tokens // block_size
+    ln_lam = math.log(lam)
+    out = np.zeros((N, Hq, D))
+    lse = np.full((N, Hq), -np.inf)
+    skip = np.zeros((N, Hkv, MB), dtype=bool)
+    gap = np.full((N, Hkv, MB), -np.inf)
+    for n in range(N):
+        L = int(seq_lens[n])
+        if L == 0:
+            continue
+        nb = (L + bs - 1) // bs
+        phys = block_table[n, :nb].astype(np.int64)
+        if np.any(phys < 0) or np.any(phys >= NB):
+            raise ValueError(f"sequence {n}: block table entry out of range")
+        t = np.arange(L)
+        for g in range(Hkv):
+            kn = k_pool[phys[t // bs], g, t % bs, :]           # [L, D]
+            vn = v_pool[phys[t // bs], g, t % bs, :]
+            s = scale * (q[n, g * G:(g + 1) * G] @ kn.T)       # [G, L]
+            # block maxima [G, nb]
+            tm = np.stack([s[:, b * bs:min(L, (b + 1) * bs)].max(axis=1) for b in range(nb)], 1)
+            keep = np.ones(L, dtype=bool)
+            for b in range(nb):
+                first = b % bps == 0
+                if first:
+                    gap[n, g, b] = np.inf
+                    continue
+                m_prev = tm[:, (b // bps) * bps:b].max(axis=1)
+                d = tm[:, b] - m_prev
+                gap[n, g, b] = float(d.max())
+                if np.all(d < ln_lam):
+                    skip[n, g, b] = True
+                    keep[b * bs:min(L, (b + 1) * bs)] = False
+            sk = np.where(keep[None, :], s, -np.inf)
+            p, l = _softmax_rows(sk)
+            out[n, g * G:(g + 1) * G] = p @ vn
+            lse[n, g * G:(g + 1) * G] = l
     return out, lse, skip, gap

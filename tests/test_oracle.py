@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import ref_prefill, ref_decode_paged, ref_blockskip, kv_head_of
+from oracle import (kv_head_of, ref_blockskip, ref_decode_paged, ref_decode_paged_blockskip,
+                    ref_prefill)
 from workloads import (decode_inputs, shared_prefix_decode_inputs, to_dtype, unshared_copy,
                        upcast_f64)
 
@@ -286,6 +287,82 @@ def test_shared_prefix_cache(layout):
                              causal=True, scale=d.scale, rows=[L - 1])
         np.testing.assert_allclose(o[n], op[0, :, 0], atol=1e-13)
         np.testing.assert_allclose(lse[n], lp[0, :, 0], atol=1e-13)
+
+
+# ------------------------------------------------------------ decode block skip
+
+def _decode_skip_replay(q, kp, vp, bt, lens, bs, scale, lam, split):
+    """Decode block skipping replayed block by block: per (sequence, K/V
+    head, split), a running max per query head over the KEPT blocks only,
+    each block tested before it is folded in; outputs from the kept tokens
+    with explicit loops.  Independent of the prefix-max formulation."""
+    N, Hq, D = q.shape
+    Hkv = kp.shape[1]
+    G = Hq // Hkv
+    ln_lam = math.log(lam)
+    out = np.zeros((N, Hq, D))
+    skip = np.zeros((N, Hkv, bt.shape[1]), dtype=bool)
+    for n in range(N):
+        L = int(lens[n])
+        for g in range(Hkv):
+            kept = []
+            for s0 in range(0, L, split):
+                m = np.full(G, -np.inf)
+                for b in range(s0 // bs, (min(L, s0 + split) + bs - 1) // bs):
+                    toks = list(range(b * bs, min(L, (b + 1) * bs)))
+                    rows = np.array([kp[bt[n, t // bs], g, t % bs] for t in toks])
+                    tm = np.array([max(scale * float(q[n, g * G + h] @ r) for r in rows)
+                                   for h in range(G)])
+                    if np.all(np.isfinite(m)) and np.all(tm - m < ln_lam):
+                        skip[n, g, b] = True
+                        continue
+                    m = np.maximum(m, tm)
+                    kept += toks
+            for h in range(g * G, (g + 1) * G):
+                sc = np.array([scale * float(q[n, h] @ kp[bt[n, t // bs], g, t % bs]) for t in kept])
+                w = np.exp(sc - sc.max())
+                w /= w.sum()
+                out[n, h] = sum(wi * vp[bt[n, t // bs], g, t % bs] for wi, t in zip(w, kept))
+    return out, skip
+
+
+@pytest.mark.parametrize("lam,amp,frac", [(1e-3, 12.0, 1 / 64), (1e-2, 6.0, 1 / 16),
+                                          (1e-3, 0.0, 0.0)])
+def test_decode_blockskip_prefix_max_equals_replay(lam, amp, frac):
+    d = decode_inputs(N=3, Hq=4, Hkv=2, D=16, seed=57, lmin=60, lmax=200, dtype="f32",
+                      sink_amplitude=amp, sink_frac=frac)
+    q, kp, vp = upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool)
+    bt, lens = d.block_table.numpy(), d.seq_lens.numpy()
+    o, lse, skip, gap = ref_decode_paged_blockskip(q, kp, vp, bt, lens, 16, d.scale, lam=lam,
+                                                   split_tokens=64)
+    ro, rskip = _decode_skip_replay(q, kp, vp, bt, lens, 16, d.scale, lam, 64)
+    np.testing.assert_array_equal(skip, rskip)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    used = gap > -np.inf
+    assert np.array_equal(skip[used], gap[used] < math.log(lam)) and not skip[~used].any()
+    if amp:
+        assert skip.sum() > 0
+    # never the first block of a split
+    assert not skip[:, :, ::4].any()
+
+
+def test_decode_blockskip_tiny_lambda_and_error_bound():
+    d = decode_inputs(N=4, Hq=8, Hkv=2, D=32, seed=58, lmin=100, lmax=700, dtype="f32",
+                      sink_amplitude=10.0, sink_frac=1 / 50)
+    args = (upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool), d.block_table.numpy(),
+            d.seq_lens.numpy(), 16, d.scale)
+    o0, l0 = ref_decode_paged(*args)
+    o1, l1, skip, _ = ref_decode_paged_blockskip(*args, lam=1e-300, split_tokens=256)
+    assert not skip.any()
+    np.testing.assert_allclose(o1, o0, atol=1e-13)      # same sums, other order
+    np.testing.assert_allclose(l1, l0, atol=1e-13)
+    o2, l2, skip, _ = ref_decode_paged_blockskip(*args, lam=1e-3, split_tokens=256)
+    assert skip.sum() > 0
+    # error bound: the dropped softmax mass, times 2 max|V|
+    dropped = 1.0 - np.exp(l2 - l0)
+    vmax = np.abs(upcast_f64(d.v_pool)).max()
+    assert np.all(np.abs(o2 - o0).max(axis=2) <= 2 * vmax * dropped + 1e-12)
+    assert dropped.max() < 1e-2
 
 
 # -------------------------------------------------------------------- blockskip

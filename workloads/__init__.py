@@ -170,7 +170,8 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
                   lmin: int = 512, lmax: int = 4096, block_size: int = 16,
                   tail: str = "zero", dtype: str = "bf16",
                   lens: Optional[list] = None,
-                  scale: Optional[float] = None, layout: str = "rowmajor") -> DecodeInputs:
+                  scale: Optional[float] = None, layout: str = "rowmajor",
+                  sink_amplitude: float = 0.0, sink_frac: float = 0.0) -> DecodeInputs:
     """Paged KV-cache decode inputs.
 
     Draw order: the N context lengths (uniform integers on [lmin, lmax],
@@ -183,6 +184,13 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
     kernel never reads).  Padding entries of the block table are -1.
     ``layout`` only rearranges elements inside each (block, head) run (see
     the module docstring); the random draws are identical for both.
+
+    With ``sink_amplitude`` > 0 (a labelled stress input for block skipping)
+    three more draws follow the permutation: one dimension kd, then for
+    each sequence a uniform draw per cached token; token 0 and the tokens
+    whose draw is below ``sink_frac`` are sinks.  The amplitude is added to
+    q[:, :, kd] and to K[sink, :, kd] before the dtype rounding, so sinks
+    dominate the scores of every query head.
     """
     rng = np.random.default_rng(seed)
     if lens is None:
@@ -203,6 +211,15 @@ def decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
         logical_k.append(rng.standard_normal((L, Hkv, D), dtype=np.float32))
         logical_v.append(rng.standard_normal((L, Hkv, D), dtype=np.float32))
     perm = rng.permutation(NB) if NB > 0 else np.zeros(0, dtype=np.int64)
+    if sink_amplitude:
+        kd = int(rng.integers(D))
+        q[:, :, kd] += np.float32(sink_amplitude)
+        for n in range(N):
+            u = rng.random(int(lens_np[n]))
+            sink = u < sink_frac
+            if len(sink):
+                sink[0] = True
+            logical_k[n][sink, :, kd] += np.float32(sink_amplitude)
     table = np.full((N, max_blocks), -1, dtype=np.int32)
     base = 0
     for n in range(N):
