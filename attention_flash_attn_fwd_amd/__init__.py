@@ -22,8 +22,8 @@ import torch
 __all__ = [
     "AttnError", "lib_path", "load", "attn_status_string", "attn_arch_supported",
     "attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
-    "attn_decode_workspace_bytes", "attn_decode_paged",
-    "prefill", "prefill_blockskip", "decode_paged",
+    "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_paged_blockskip",
+    "prefill", "prefill_blockskip", "decode_paged", "decode_paged_blockskip",
 ]
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -68,6 +68,10 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged.restype = _I
     lib.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                       _F, _P, ctypes.c_size_t, _P]
+    lib.attn_decode_paged_blockskip.restype = _I
+    lib.attn_decode_paged_blockskip.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I,
+                                                _I, _I, _I, _F, _F, _P, _P, _P, ctypes.c_size_t,
+                                                _P]
     _LIB = lib
     return lib
 
@@ -184,10 +188,8 @@ def _pool_shapes(NB, Hkv, bs, D, layout):
     return (NB, Hkv, D // 8, bs, 8), (NB, Hkv, D, bs)
 
 
-def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o, lse,
-                      scale: float, workspace, stream=None, layout: str = "rowmajor") -> None:
-    """Paged decode into caller-allocated o [N,Hq,D] and lse [N,Hq] (or None).
-    ``layout`` names the pool layout: "rowmajor" or "mfma" (see include/attn.h)."""
+def _decode_check(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse, workspace,
+                  layout):
     N, Hq, D = q.shape
     NB, Hkv = k_pool.shape[0], k_pool.shape[1]
     _dev(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace)
@@ -202,13 +204,44 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int,
         raise ValueError("block_table must be [N, max_blocks], seq_lens [N]")
     if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq)):
         raise ValueError("lse must be float32 [N,Hq]")
-    nbytes = workspace.numel() * workspace.element_size()
+    return N, Hq, Hkv, D, NB, workspace.numel() * workspace.element_size()
+
+
+def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o, lse,
+                      scale: float, workspace, stream=None, layout: str = "rowmajor") -> None:
+    """Paged decode into caller-allocated o [N,Hq,D] and lse [N,Hq] (or None).
+    ``layout`` names the pool layout: "rowmajor" or "mfma" (see include/attn.h)."""
+    N, Hq, Hkv, D, NB, nbytes = _decode_check(q, k_pool, v_pool, block_table, seq_lens,
+                                              block_size, o, lse, workspace, layout)
     st = load().attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                   _ptr(seq_lens), int(block_size), KV_LAYOUTS[layout], _ptr(o),
                                   _ptr(lse), N, Hq, Hkv,
                                   D, NB, int(block_table.shape[1]), float(scale), _ptr(workspace),
                                   nbytes, _stream(stream))
     _check(st, "attn_decode_paged")
+
+
+def attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o,
+                                lse, scale: float, lam: float, workspace, skip_bitmap=None,
+                                skipped_blocks=None, stream=None, layout: str = "mfma") -> None:
+    """Paged decode with block skipping (MFMA-native pools); skip_bitmap is
+    uint8 [N, Hkv, max_blocks] or None, skipped_blocks one 64-bit device
+    integer (incremented) or None."""
+    N, Hq, Hkv, D, NB, nbytes = _decode_check(q, k_pool, v_pool, block_table, seq_lens,
+                                              block_size, o, lse, workspace, layout)
+    MB = int(block_table.shape[1])
+    _dev(skip_bitmap, skipped_blocks)
+    if skip_bitmap is not None and (skip_bitmap.dtype != torch.uint8
+                                    or skip_bitmap.shape != (N, Hkv, MB)):
+        raise ValueError("skip_bitmap must be uint8 [N, Hkv, max_blocks]")
+    if skipped_blocks is not None and (skipped_blocks.numel() != 1
+                                       or skipped_blocks.element_size() != 8):
+        raise ValueError("skipped_blocks must be one 64-bit integer")
+    st = load().attn_decode_paged_blockskip(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), int(block_size),
+        KV_LAYOUTS[layout], _ptr(o), _ptr(lse), N, Hq, Hkv, D, NB, MB, float(scale), float(lam),
+        _ptr(skip_bitmap), _ptr(skipped_blocks), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "attn_decode_paged_blockskip")
 
 
 # ------------------------------------------------------ allocating wrappers
@@ -257,3 +290,24 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int = 16,
     attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse, scale,
                       workspace, layout=layout)
     return o, lse
+
+
+def decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, lam: float,
+                           block_size: int = 16, scale: Optional[float] = None, workspace=None):
+    """Allocate O, LSE, the skip bitmap and counter (and the workspace unless
+    given) and run the block-skip paged decode on MFMA-native pools.
+    Returns (o, lse, skip_bitmap, skipped_blocks)."""
+    N, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    bm = torch.zeros((N, Hkv, int(block_table.shape[1])), dtype=torch.uint8, device=q.device)
+    cnt = torch.zeros(1, dtype=torch.int64, device=q.device)
+    if workspace is None:
+        nbytes = attn_decode_workspace_bytes(N, Hq, D, int(block_table.shape[1]), block_size)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse,
+                                scale, lam, workspace, bm, cnt, layout="mfma")
+    return o, lse, bm, cnt

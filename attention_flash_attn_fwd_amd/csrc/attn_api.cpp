@@ -114,17 +114,24 @@ size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_blocks_p
   return (size_t)num_seqs * Hq * ns * ((size_t)D + 1) * sizeof(float);
 }
 
-int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
-                      const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                      int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D, int num_blocks,
-                      int max_blocks_per_seq, float scale, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_common(const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                  int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
+                  int num_blocks, int max_blocks_per_seq, float scale, void* workspace,
+                  size_t workspace_bytes, int skip, float lambda, uint8_t* skip_bitmap,
+                  unsigned long long* skipped_blocks, hipStream_t stream) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
     return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (!finite_pos(scale)) return ATTN_ERR_INVALID_ARG;
   if (kv_layout != ATTN_KV_ROWMAJOR && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_INVALID_ARG;
+  if (skip && !(lambda > 0.f && lambda < 1.f)) return ATTN_ERR_INVALID_ARG;
+  if (skip && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_UNSUPPORTED;
   if (block_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
@@ -154,10 +161,40 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks = max_blocks_per_seq;
   a.layout = kv_layout;
   a.scale = scale;
+  a.skip = skip;
+  a.lambda = lambda;
+  a.skip_bitmap = skip_bitmap;
+  a.skip_count = skipped_blocks;
   a.n_split = ns;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = a.ws_o + (size_t)num_seqs * Hq * ns * D;
   return hip_status(attn::launch_decode_paged(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                      int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
+                      int num_blocks, int max_blocks_per_seq, float scale, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, kv_layout, o, lse,
+                       num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, workspace,
+                       workspace_bytes, 0, 0.f, nullptr, nullptr, stream);
+}
+
+int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int kv_layout, void* o, float* lse, int num_seqs,
+                                int Hq, int Hkv, int D, int num_blocks, int max_blocks_per_seq,
+                                float scale, float lambda, uint8_t* skip_bitmap,
+                                unsigned long long* skipped_blocks, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, kv_layout, o, lse,
+                       num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, workspace,
+                       workspace_bytes, 1, lambda, skip_bitmap, skipped_blocks, stream);
 }
 
 }  // extern "C"

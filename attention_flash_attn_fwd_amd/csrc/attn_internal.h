@@ -40,6 +40,11 @@ struct DecodeArgs {
   int N, Hq, Hkv, D, block_size, num_blocks, max_blocks;
   int layout;  // 0 row-major pools, 1 MFMA-native pools
   float scale;
+  // block skip (ignored unless skip != 0; MFMA-native pools only)
+  int skip;
+  float lambda;
+  uint8_t* skip_bitmap;            // may be null
+  unsigned long long* skip_count;  // may be null
   float* ws_o;    // [N, Hq, n_split, D]
   float* ws_lse;  // [N, Hq, n_split]
   int n_split;

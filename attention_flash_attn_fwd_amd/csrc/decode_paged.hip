@@ -63,6 +63,10 @@ struct DecParams {
   float* ws_lse;
   int Hq, Hkv, G, num_blocks, max_blocks, n_split;
   float sl2;
+  // block skip only
+  float thr;                       // log2(lambda)
+  uint8_t* skip_map;               // [N, Hkv, max_blocks] or null
+  unsigned long long* skip_count;  // or null
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -476,6 +480,216 @@ __global__ __launch_bounds__(64, kDecodeWavesPerSimd) void decode_native_kernel(
   }
 }
 
+// Decode with block skipping ("高效部署稀疏注意力加速方案：BLASST方法详解与实践
+// 指南", 架构与组件: blocks whose scores are negligible next to the running
+// maximum of the blockwise online softmax lose their exp, their V load and
+// their matrix product), on MFMA-native pools.  Inside a split the pool
+// blocks are walked in order; for every query head h of the K/V group the
+// block maximum tm_h is compared with the running maximum m_h of the
+// split's earlier blocks, and the block is skipped when tm_h - m_h < log2
+// lambda for all h (the V block is shared by the group).  The split's first
+// block is always kept.  The V load is the decode's cost, so it is issued
+// only after the decision: K runs two blocks ahead, the block's scores and
+// decision come next, its V is loaded if kept and consumed one step later.
+// The loop is unrolled six times so that the three K and two V buffers have
+// fixed registers (moving a register whose load is in flight would wait).
+template <int D>
+__global__ __launch_bounds__(64, kDecodeWavesPerSimd) void decode_skip_kernel(DecParams p) {
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int RUN = kBlk * D * 2;
+
+  const int kvh = blockIdx.x, split = blockIdx.y, n = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int h = lane & 15, g4 = lane >> 4;
+  const int L = p.seq_lens[n];
+  const int tok_begin = split * kDecodeSplitTokens;
+  if (L <= 0 || tok_begin >= L) return;
+  const int n_tok = min(L - tok_begin, kDecodeSplitTokens);
+  const int G = p.G;
+
+  const int32_t* trow = p.table + (size_t)n * p.max_blocks;
+  const int lb0 = tok_begin / kBlk;
+  const int n_blk = (n_tok + kBlk - 1) / kBlk;
+  const bool in_table = lb0 + n_blk <= p.max_blocks;
+  int my_ph = 0;
+  if (in_table && lane < n_blk) my_ph = trow[lb0 + lane];
+  bf16x8 qB[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (h < G)
+      qB[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)n * p.Hq + kvh * G + h) * D +
+                                                ks * 32 + g4 * 8);
+    else
+      qB[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  const bool lane_ok = lane >= n_blk || (my_ph >= 0 && my_ph < p.num_blocks);
+  const bool bad = !in_table || !__all(lane_ok);
+  const size_t slot = ((size_t)n * p.Hq + kvh * G + h) * p.n_split + split;
+  if (bad) {
+    if (h < G) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = f32x4{NAN, NAN, NAN, NAN};
+      if (g4 == 0) p.ws_lse[slot] = NAN;
+    }
+    return;
+  }
+
+  const size_t blk_stride = (size_t)p.Hkv * RUN;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k_pool) + (size_t)kvh * RUN;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v_pool) + (size_t)kvh * RUN;
+  const uint32_t k_off = (uint32_t)((g4 * 16 + h) * 16);
+  const uint32_t v_off = (uint32_t)((h * 16 + 4 * g4) * 2);
+  auto load_k = [&](int j, bf16x8* kb) {
+    const size_t ph = (size_t)__builtin_amdgcn_readlane(my_ph, j);
+    const unsigned char* src = kbase + ph * blk_stride + k_off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kb[ks] = __builtin_bit_cast(
+          bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ks * 1024)));
+  };
+  auto load_v = [&](int j, s16x4* vb) {
+    const size_t ph = (size_t)__builtin_amdgcn_readlane(my_ph, j);
+    const unsigned char* src = vbase + ph * blk_stride + v_off;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vb[db] = __builtin_bit_cast(
+          s16x4, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + db * 512)));
+  };
+
+  const float sl2 = p.sl2;
+  // raw scores S^T of block j (tail slots -inf) and their per-head maximum
+  auto scores = [&](int j, const bf16x8* kb) -> f32x4 {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qB[ks], s, 0, 0, 0);
+    // branch-free tail mask: the first reads of the MFMA result stay in the
+    // MFMA's basic block, where the compiler counts the wait states a VALU
+    // read of an MFMA result needs (across a branch they were not counted)
+    const int valid = n_tok - j * kBlk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = 4 * g4 + i < valid ? s[i] : -INFINITY;
+    return s;
+  };
+  auto block_max = [&](const f32x4& s) -> float {
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    return half_swap_max(mx) * sl2;
+  };
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_used = kUnset, l = 0.f;
+  float m_true = kUnset;  // running max of the split's earlier blocks (log2 units)
+  unsigned skipped = 0;
+  // skip decision for block j (j = 0 is the split's first block: kept)
+  auto decide = [&](int j, float tmx) -> bool {
+    bool neg = true;  // padding columns (h >= G) never keep a block
+    if (h < G) neg = m_true > 0.5f * kUnset && tmx - m_true < p.thr;
+    const bool sk = j > 0 && __all(neg);
+    m_true = fmaxf(m_true, tmx);
+    if (lane == 0 && p.skip_map)
+      p.skip_map[((size_t)n * p.Hkv + kvh) * p.max_blocks + lb0 + j] = sk ? 1 : 0;
+    skipped += sk ? 1u : 0u;
+    return sk;
+  };
+  // softmax and O^T += V^T P^T of a kept block
+  auto finish = [&](int j, f32x4 s, float tmx, s16x4* vb) {
+    const int valid = n_tok - j * kBlk;
+    if (valid < kBlk) {
+      uint32_t keep[2];
+      keep[0] = (4 * g4 + 0 < valid ? 0xffffu : 0u) | (4 * g4 + 1 < valid ? 0xffff0000u : 0u);
+      keep[1] = (4 * g4 + 2 < valid ? 0xffffu : 0u) | (4 * g4 + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        u32x2 w = __builtin_bit_cast(u32x2, vb[db]);
+        w[0] &= keep[0];
+        w[1] &= keep[1];
+        vb[db] = __builtin_bit_cast(s16x4, w);
+      }
+    }
+    if (__any(tmx > m_used + 8.f)) {
+      const float m_new = fmaxf(m_used, tmx);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float nm = -m_used;
+    const uint32_t pk0 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[0], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[1], sl2, nm)));
+    const uint32_t pk1 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[2], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[3], sl2, nm)));
+    l += __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk0), kOnes2, 0.f, false) +
+         __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk1), kOnes2, 0.f, false);
+    const u32x2 pw = {pk0, pk1};
+    const s16x4 pB = __builtin_bit_cast(s16x4, pw);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb[db], pB, acc[db], 0, 0, 0);
+  };
+
+  bf16x8 k0[NKS], k1[NKS], k2[NKS];
+  s16x4 v0[NDB], v1[NDB];
+  f32x4 s_cur;
+  float t_cur;
+  bool keep_cur;
+  // step j: score and decide block j+1 (its K has arrived), load its V if
+  // kept and the K of block j+3 into the buffer block j used; then finish
+  // block j with the V loaded one step earlier
+  auto step = [&](int j, const bf16x8* ksc, bf16x8* kld, s16x4* vcur, s16x4* vnxt) {
+    f32x4 s_n = {0.f, 0.f, 0.f, 0.f};
+    float t_n = 0.f;
+    bool keep_n = false;
+    if (j + 1 < n_blk) {
+      s_n = scores(j + 1, ksc);
+      t_n = block_max(s_n);
+      keep_n = !decide(j + 1, t_n);
+      if (keep_n) load_v(j + 1, vnxt);
+      if (j + 3 < n_blk) load_k(j + 3, kld);
+    }
+    if (keep_cur) finish(j, s_cur, t_cur, vcur);
+    s_cur = s_n;
+    t_cur = t_n;
+    keep_cur = keep_n;
+  };
+  load_k(0, k0);
+  if (n_blk > 1) load_k(1, k1);
+  s_cur = scores(0, k0);
+  t_cur = block_max(s_cur);
+  keep_cur = !decide(0, t_cur);
+  load_v(0, v0);
+  if (n_blk > 2) load_k(2, k2);
+  for (int j = 0; j < n_blk; j += 6) {
+    step(j, k1, k0, v0, v1);
+    if (j + 1 >= n_blk) break;
+    step(j + 1, k2, k1, v1, v0);
+    if (j + 2 >= n_blk) break;
+    step(j + 2, k0, k2, v0, v1);
+    if (j + 3 >= n_blk) break;
+    step(j + 3, k1, k0, v1, v0);
+    if (j + 4 >= n_blk) break;
+    step(j + 4, k2, k1, v0, v1);
+    if (j + 5 >= n_blk) break;
+    step(j + 5, k0, k2, v1, v0);
+  }
+
+  if (lane == 0 && skipped && p.skip_count)
+    atomicAdd(p.skip_count, (unsigned long long)skipped);
+  float lt = l + __shfl_xor(l, 16);
+  lt = half_swap_add(lt);
+  if (h < G) {
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = acc[db] * inv;
+    if (g4 == 0) p.ws_lse[slot] = m_used + __log2f(lt);
+  }
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
@@ -537,8 +751,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const DecParams& p, int N, int layout, hipStream_t stream) {
-  if (layout == 1)
+hipError_t launch_d(const DecParams& p, int N, int layout, bool skip, hipStream_t stream) {
+  if (skip)
+    hipLaunchKernelGGL((decode_skip_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
+  else if (layout == 1)
     hipLaunchKernelGGL((decode_native_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_split_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
@@ -568,8 +784,14 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.n_split = a.n_split;
   p.sl2 = a.scale * 1.4426950408889634f;
   p.G = a.Hq / a.Hkv;
+  p.thr = a.skip ? (float)(log((double)a.lambda) * 1.4426950408889634) : 0.f;
+  p.skip_map = a.skip_bitmap;
+  p.skip_count = a.skip_count;
   if (p.G > 16) return hipErrorInvalidValue;
-  return a.D == 64 ? launch_d<64>(p, a.N, a.layout, stream) : launch_d<128>(p, a.N, a.layout, stream);
+  if (a.skip && a.layout != 1) return hipErrorInvalidValue;
+  const bool sk = a.skip != 0;
+  return a.D == 64 ? launch_d<64>(p, a.N, a.layout, sk, stream)
+                   : launch_d<128>(p, a.N, a.layout, sk, stream);
 }
 
 }  // namespace attn

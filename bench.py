@@ -217,6 +217,47 @@ def main():
             "note": "16 prompts x 4 samples, 1536-token shared prompt, U[1,2048] own tokens"}
         del spools
 
+        # block skip inside the decode: the decode workload itself, and a
+        # labelled stress input with attention sinks (amplitude 12 on a seeded
+        # dimension at token 0 and 1/64 of the cached tokens), lambda 1e-3
+        for label, amp in (("paged_decode_blockskip", 0.0),
+                           ("paged_decode_blockskip_stress_sinks", 12.0)):
+            wb = decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"],
+                               lmin=cd["lmin"], lmax=cd["lmax"], layout="mfma",
+                               sink_amplitude=amp, sink_frac=1 / 64 if amp else 0.0)
+            bq, bbt, bsl = wb.q.to(dev), wb.block_table.to(dev), wb.seq_lens.to(dev)
+            bpools = [(wb.k_pool.to(dev), wb.v_pool.to(dev)) for _ in range(2)]
+            bcnt = torch.zeros(1, dtype=torch.int64, device=dev)
+            bctr = [0]
+
+            def run_dense():
+                kp, vp = bpools[bctr[0] % 2]
+                bctr[0] += 1
+                A.attn_decode_paged(bq, kp, vp, bbt, bsl, 16, do, dlse, wb.scale, ws, layout="mfma")
+
+            def run_skip():
+                kp, vp = bpools[bctr[0] % 2]
+                bctr[0] += 1
+                A.attn_decode_paged_blockskip(bq, kp, vp, bbt, bsl, 16, do, dlse, wb.scale, 1e-3,
+                                              ws, None, None, layout="mfma")
+            md = time_it(run_dense, 20)
+            mk = time_it(run_skip, 20)
+            bcnt.zero_()
+            A.attn_decode_paged_blockskip(bq, *bpools[0], bbt, bsl, 16, do, dlse, wb.scale, 1e-3,
+                                          ws, None, bcnt, layout="mfma")
+            torch.cuda.synchronize()
+            blocks = int(((wb.seq_lens.to(torch.int64) + 15) // 16).sum()) * cd["Hkv"]
+            frac = int(bcnt.item()) / blocks
+            kvb = wb.kv_bytes()
+            secondary[label] = {
+                "skipped_fraction": round(frac, 6), "skipped_blocks": int(bcnt.item()),
+                "blocks": blocks, "lambda": 1e-3,
+                "us_per_launch": round(mk * 1e6, 2), "dense_us_per_launch": round(md * 1e6, 2),
+                "speedup_vs_dense": round(md / mk, 3),
+                "logical_kv_GBps": round(kvb / mk / 1e9, 1),
+                "read_kv_GBps": round(kvb * (1 - 0.5 * frac) / mk / 1e9, 1)}
+            del bpools
+
         c3 = CONFIGS["gqa_causal_s8192"]
         w3 = prefill_inputs(c3["B"], c3["Hq"], c3["Hkv"], c3["S"], c3["D"], seed=c3["seed"])
         q3, k3, v3 = w3.q.to(dev), w3.k.to(dev), w3.v.to(dev)

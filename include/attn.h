@@ -184,6 +184,34 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       int num_blocks, int max_blocks_per_seq, float scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Paged decode with block skipping ("高效部署稀疏注意力加速方案：BLASST方法详解与
+ * 实践指南", 架构与组件: a running maximum from the blockwise online softmax and
+ * a threshold lambda decide which blocks matter; the others lose their exp,
+ * their V load and their matrix product).  Arguments as attn_decode_paged,
+ * plus:
+ *   kv_layout     : must be ATTN_KV_MFMA (ATTN_ERR_UNSUPPORTED otherwise)
+ *   lambda        : threshold, 0 < lambda < 1
+ *   skip_bitmap   : uint8 [N, Hkv, max_blocks_per_seq] or NULL; entry
+ *                   (n, g, j) is set to 1 if logical block j of sequence n
+ *                   was skipped for K/V head g, 0 if kept; entries past the
+ *                   sequence are not written
+ *   skipped_blocks: device counter or NULL, incremented by the number of
+ *                   skipped (sequence, K/V head, block) triples; the caller
+ *                   zeroes it
+ * Rule: each sequence's tokens are cut into the same 512-token splits as
+ * the split-KV decode; inside a split the blocks are taken in order, and
+ * block j is skipped when for every query head h of the K/V group its
+ * maximum scaled score minus the maximum over the split's earlier blocks is
+ * below ln(lambda).  A split's first block is always kept.  O and LSE are
+ * the attention over the kept blocks' tokens. */
+int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int block_size, int kv_layout, void* o, float* lse, int num_seqs,
+                                int Hq, int Hkv, int D, int num_blocks, int max_blocks_per_seq,
+                                float scale, float lambda, uint8_t* skip_bitmap,
+                                unsigned long long* skipped_blocks, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

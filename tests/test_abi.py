@@ -25,8 +25,8 @@ def _declared():
 def test_header_lists_the_entry_points():
     names = _declared()
     for need in ("attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
-                 "attn_decode_paged", "attn_decode_workspace_bytes", "attn_status_string",
-                 "attn_arch_supported"):
+                 "attn_decode_paged", "attn_decode_paged_blockskip",
+                 "attn_decode_workspace_bytes", "attn_status_string", "attn_arch_supported"):
         assert need in names
 
 
@@ -115,3 +115,25 @@ def test_decode_workspace_and_validation_without_device():
     assert call(ws=None) == -4
     assert call(wsb=need - 1) == -4
     assert call(ws=260) == -4                # misaligned workspace
+
+
+def test_decode_blockskip_validation_without_device():
+    lib = A.load()
+    need = A.attn_decode_workspace_bytes(2, 8, 128, 4, 16)
+
+    def call(**kw):
+        a = dict(q=8, kp=8, vp=8, bt=8, sl=8, bs=16, lay=1, o=8, N=2, Hq=8, Hkv=2, D=128, NB=8,
+                 MB=4, scale=0.1, lam=1e-3, ws=256, wsb=need)
+        a.update(kw)
+        return lib.attn_decode_paged_blockskip(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["bs"],
+                                               a["lay"], a["o"], None, a["N"], a["Hq"], a["Hkv"],
+                                               a["D"], a["NB"], a["MB"], a["scale"], a["lam"],
+                                               None, None, a["ws"], a["wsb"], None)
+    assert call(lam=0.0) == -1
+    assert call(lam=1.0) == -1
+    assert call(lam=float("nan")) == -1
+    assert call(lay=0) == -2            # row-major pools: not supported with block skip
+    assert call(lay=3) == -1
+    assert call(bt=None) == -1
+    assert call(D=96) == -2
+    assert call(ws=None) == -4

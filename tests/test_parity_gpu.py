@@ -7,6 +7,7 @@ oracle's on every tile whose decision margin |gap - ln(lambda)| is at least
 1e-3 (the oracle's gap is fp64, the kernel's fp32; tiles inside that margin
 are reported, and none occur in the seeded workloads below).
 """
+import dataclasses
 import math
 import sys
 
@@ -15,7 +16,7 @@ import pytest
 import torch
 
 import attention_flash_attn_fwd_amd as A
-from oracle import ref_blockskip, ref_decode_paged, ref_prefill
+from oracle import ref_blockskip, ref_decode_paged, ref_decode_paged_blockskip, ref_prefill
 from workloads import (CONFIGS, blockskip_inputs, decode_inputs, prefill_inputs,
                        shared_prefix_decode_inputs, unshared_copy, upcast_f64)
 
@@ -203,6 +204,67 @@ def test_paged_decode_shared_prefix(layout):
     # the same logical cache without sharing gives the identical bits
     o2, l2 = _run_decode(unshared_copy(d))
     assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+# ---------------------------------------------------------- decode block skip
+
+SPLIT = 512  # tokens per split of the split-KV decode
+
+
+def _run_decode_skip(d, lam):
+    q, kp, vp = d.q.cuda(), d.k_pool.cuda(), d.v_pool.cuda()
+    o, lse, bm, cnt = A.decode_paged_blockskip(q, kp, vp, d.block_table.cuda(),
+                                               d.seq_lens.cuda(), lam, scale=d.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), bm.cpu().numpy(), int(cnt.item())
+
+
+def _check_decode_skip(d, lam, what, min_frac=0.0):
+    o, lse, bm, cnt = _run_decode_skip(d, lam)
+    ro, rl, skip, gap = ref_decode_paged_blockskip(
+        upcast_f64(d.q), upcast_f64(d.k_pool), upcast_f64(d.v_pool), d.block_table.numpy(),
+        d.seq_lens.numpy(), 16, d.scale, lam=lam, split_tokens=SPLIT, layout=d.layout)
+    used = gap > -np.inf
+    border = used & (np.abs(gap - math.log(lam)) < 1e-3)
+    mism = used & ~border & (bm.astype(bool) != skip)
+    say(f"{what}: skipped {int(skip.sum())}/{int(used.sum())} blocks, borderline "
+        f"{int(border.sum())}, mismatches {int(mism.sum())}")
+    assert mism.sum() == 0
+    assert cnt == int(bm[used].astype(np.int64).sum())
+    assert skip.sum() >= min_frac * used.sum()
+    _compare(o, lse, ro, rl, TOL["bf16"], what)
+    return o, lse
+
+
+def test_decode_blockskip_stress_decisions():
+    say("decode block skip: sink stress input, lambda 1e-3")
+    d = decode_inputs(16, 32, 8, 128, seed=97, lmin=100, lmax=3000, tail="nan", layout="mfma",
+                      sink_amplitude=12.0, sink_frac=1 / 64)
+    _check_decode_skip(d, 1e-3, "decode skip stress", min_frac=0.2)
+
+
+def test_decode_blockskip_tiny_lambda_matches_dense():
+    say("decode block skip with lambda=1e-30: nothing skipped, equals the dense decode")
+    d = decode_inputs(8, 32, 8, 128, seed=98, lmin=1, lmax=2000, tail="nan", layout="mfma")
+    o, lse, bm, cnt = _run_decode_skip(d, 1e-30)
+    assert cnt == 0 and bm.sum() == 0
+    od, ld = _run_decode(d)
+    _compare(o, lse, od.astype(np.float64), ld.astype(np.float64), TOL["bf16"], "skip vs dense")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 1, 64), (8, 8, 128), (32, 2, 128)])
+def test_decode_blockskip_edge_lengths(Hq, Hkv, D):
+    lens = [1, 16, 17, 511, 512, 513, 1000, 0, 1024, 1537]
+    say(f"decode block skip edge lengths Hq{Hq} Hkv{Hkv} D{D}")
+    d = decode_inputs(len(lens), Hq, Hkv, D, seed=99 + D, lens=lens, tail="nan", layout="mfma",
+                      sink_amplitude=12.0, sink_frac=1 / 32)
+    o, lse, bm, cnt = _run_decode_skip(d, 1e-3)
+    z = lens.index(0)
+    assert np.all(o[z] == 0) and np.all(np.isneginf(lse[z]))
+    keep = [i for i in range(len(lens)) if lens[i] > 0]
+    dk = dataclasses.replace(d, q=d.q[keep], block_table=d.block_table[keep],
+                             seq_lens=d.seq_lens[keep], N=len(keep))
+    _check_decode_skip(dk, 1e-3, f"decode skip edges Hq{Hq} Hkv{Hkv} D{D}")
 
 
 # ---------------------------------------------------------------- block skip
