@@ -15,4 +15,5 @@ from .attention import (  # noqa: F401
     kv_head_of,
     pool_rows,
     ref_decode_paged_blockskip,
+    ref_prefill_paged,
 )

@@ -44,7 +44,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip", "pool_rows",
-           "ref_decode_paged_blockskip"]
+           "ref_decode_paged_blockskip", "ref_prefill_paged"]
 
 
 def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
@@ -306,3 +306,48 @@ def ref_decode_paged_blockskip(q: np.ndarray, k_pool: np.ndarray, v_pool: np.nda
             out[n, g * G:(g + 1) * G] = p @ vn
             lse[n, g * G:(g + 1) * G] = l
     return out, lse, skip, gap
+
+
+def ref_prefill_paged(q: np.ndarray, cu_seqlens_q: np.ndarray, k_pool: np.ndarray,
+                      v_pool: np.ndarray, block_table: np.ndarray, seq_lens_k: np.ndarray,
+                      block_size: int, scale: float, layout: str = "rowmajor"):
+    """Chunked / variable-length prefill over the paged KV cache [KV] (the
+    prefill-with-KV-cache case of the FlashAttention integration page).
+
+    Sequence n has Sk = seq_lens_k[n] tokens whose K/V are in the pool
+    (gathered through its block-table row as in :func:`ref_decode_paged`);
+    its Sq = cu_seqlens_q[n+1] - cu_seqlens_q[n] queries, rows
+    cu_seqlens_q[n] .. of the packed q [total_q, Hq, D], are its LAST Sq
+    positions: query i sits at position Sk - Sq + i and sees the keys
+    j <= Sk - Sq + i (causal, bottom-right aligned).
+    Returns (O [total_q, Hq, D], LSE [total_q, Hq]).
+    """
+    k_pool = pool_rows(k_pool, layout, "k")
+    v_pool = pool_rows(v_pool, layout, "v")
+    total_q, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_pool.shape
+    N = len(seq_lens_k)
+    out = np.zeros((total_q, Hq, D))
+    lse = np.zeros((total_q, Hq))
+    for n in range(N):
+        r0, r1 = int(cu_seqlens_q[n]), int(cu_seqlens_q[n + 1])
+        Sq, Sk = r1 - r0, int(seq_lens_k[n])
+        if Sq == 0:
+            continue
+        if Sq > Sk:
+            raise ValueError(f"sequence {n}: more queries than cached tokens")
+        t = np.arange(Sk)
+        phys = block_table[n, t // bs].astype(np.int64)
+        if np.any(phys < 0) or np.any(phys >= NB):
+            raise ValueError(f"sequence {n}: block table entry out of range")
+        pos = Sk - Sq + np.arange(Sq)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            kn = k_pool[phys, g, t % bs, :]
+            vn = v_pool[phys, g, t % bs, :]
+            s = scale * (q[r0:r1, h, :] @ kn.T)                     # [Sq, Sk]
+            s = np.where(t[None, :] <= pos[:, None], s, -np.inf)
+            p, l = _softmax_rows(s)
+            out[r0:r1, h] = p @ vn
+            lse[r0:r1, h] = l
+    return out, lse

@@ -10,9 +10,9 @@ import pytest
 import torch
 
 from oracle import (kv_head_of, ref_blockskip, ref_decode_paged, ref_decode_paged_blockskip,
-                    ref_prefill)
-from workloads import (decode_inputs, shared_prefix_decode_inputs, to_dtype, unshared_copy,
-                       upcast_f64)
+                    ref_prefill, ref_prefill_paged)
+from workloads import (decode_inputs, paged_prefill_inputs, shared_prefix_decode_inputs,
+                       to_dtype, unshared_copy, upcast_f64)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -287,6 +287,76 @@ def test_shared_prefix_cache(layout):
                              causal=True, scale=d.scale, rows=[L - 1])
         np.testing.assert_allclose(o[n], op[0, :, 0], atol=1e-13)
         np.testing.assert_allclose(lse[n], lp[0, :, 0], atol=1e-13)
+
+
+# ------------------------------------------------------- chunked paged prefill
+
+def _logical_kv(ctx, ql, Hq, Hkv, D, seed):
+    """Re-draw the generator's logical K/V (documented draw order: packed q,
+    then per sequence K then V), independent of the pool and the table."""
+    rng = np.random.default_rng(seed)
+    rng.standard_normal((int(sum(ql)), Hq, D), dtype=np.float32)
+    out = []
+    for c, qn in zip(ctx, ql):
+        L = c + qn
+        k = rng.standard_normal((L, Hkv, D), dtype=np.float32)
+        v = rng.standard_normal((L, Hkv, D), dtype=np.float32)
+        out.append((upcast_f64(to_dtype(k, "f32")), upcast_f64(to_dtype(v, "f32"))))
+    return out
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "mfma"])
+def test_paged_prefill_chunks_are_rows_of_the_full_prefill(layout):
+    ctx, ql = [0, 37, 100, 5], [20, 1, 70, 33]
+    d = paged_prefill_inputs(ctx, ql, 4, 2, 16, seed=61, dtype="f32", tail="nan", layout=layout)
+    q = upcast_f64(d.q)
+    o, lse = ref_prefill_paged(q, d.cu_seqlens_q.numpy(), upcast_f64(d.k_pool),
+                               upcast_f64(d.v_pool), d.block_table.numpy(),
+                               d.seq_lens_k.numpy(), 16, d.scale, layout=layout)
+    cu = d.cu_seqlens_q.numpy()
+    for n, (K, V) in enumerate(_logical_kv(ctx, ql, 4, 2, 16, 61)):
+        L = K.shape[0]
+        qq = np.zeros((1, 4, L, 16))
+        qq[0, :, ctx[n]:] = q[cu[n]:cu[n + 1]].transpose(1, 0, 2)
+        rows = np.arange(ctx[n], L)
+        of, lf = ref_prefill(qq, K.transpose(1, 0, 2)[None], V.transpose(1, 0, 2)[None],
+                             causal=True, scale=d.scale, rows=rows)
+        np.testing.assert_allclose(o[cu[n]:cu[n + 1]], of[0].transpose(1, 0, 2), atol=1e-13)
+        np.testing.assert_allclose(lse[cu[n]:cu[n + 1]], lf[0].T, atol=1e-13)
+
+
+def test_paged_prefill_single_token_chunk_is_decode():
+    ctx = [3, 50, 200]
+    d = paged_prefill_inputs(ctx, [1, 1, 1], 8, 2, 16, seed=62, dtype="f32")
+    args = (upcast_f64(d.k_pool), upcast_f64(d.v_pool), d.block_table.numpy())
+    o, lse = ref_prefill_paged(upcast_f64(d.q), d.cu_seqlens_q.numpy(), *args,
+                               d.seq_lens_k.numpy(), 16, d.scale)
+    od, ld = ref_decode_paged(upcast_f64(d.q), *args, d.seq_lens_k.numpy(), 16, d.scale)
+    np.testing.assert_allclose(o, od, atol=1e-13)
+    np.testing.assert_allclose(lse, ld, atol=1e-13)
+
+
+def test_paged_prefill_brute_force_tiny():
+    ctx, ql = [2, 0], [3, 2]
+    d = paged_prefill_inputs(ctx, ql, 2, 1, 4, seed=63, dtype="f32", block_size=16)
+    q = upcast_f64(d.q)
+    o, _ = ref_prefill_paged(q, d.cu_seqlens_q.numpy(), upcast_f64(d.k_pool),
+                             upcast_f64(d.v_pool), d.block_table.numpy(), d.seq_lens_k.numpy(),
+                             16, d.scale)
+    logical = _logical_kv(ctx, ql, 2, 1, 4, 63)
+    r = 0
+    for n in range(2):
+        K, V = logical[n]
+        for i in range(ql[n]):
+            pos = ctx[n] + i
+            for h in range(2):
+                w = [math.exp(d.scale * sum(q[r, h, x] * K[j, 0, x] for x in range(4)))
+                     for j in range(pos + 1)]
+                z = sum(w)
+                for x in range(4):
+                    ref = sum(w[j] * V[j, 0, x] for j in range(pos + 1)) / z
+                    assert abs(o[r, h, x] - ref) < 1e-12
+            r += 1
 
 
 # ------------------------------------------------------------ decode block skip

@@ -40,7 +40,7 @@ import torch
 __all__ = [
     "PrefillInputs", "DecodeInputs", "CONFIGS",
     "prefill_inputs", "blockskip_inputs", "decode_inputs", "shared_prefix_decode_inputs",
-    "unshared_copy", "to_dtype",
+    "unshared_copy", "paged_prefill_inputs", "PagedPrefillInputs", "to_dtype",
     "upcast_f64", "prefill_flops",
 ]
 
@@ -321,6 +321,84 @@ def shared_prefix_decode_inputs(n_prompts: int, n_samples: int, Hq: int, Hkv: in
         block_size=bs, N=N, Hq=Hq, Hkv=Hkv, D=D, max_blocks=max_blocks,
         scale=float(scale), dtype=dtype, seed=seed, perm=perm, layout=layout)
     return d, logical
+
+
+@dataclasses.dataclass
+class PagedPrefillInputs:
+    q: torch.Tensor             # [total_q, Hq, D] packed queries
+    cu_seqlens_q: torch.Tensor  # int32 [N + 1]
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    block_table: torch.Tensor   # int32 [N, max_blocks]
+    seq_lens_k: torch.Tensor    # int32 [N]
+    block_size: int
+    N: int
+    Hq: int
+    Hkv: int
+    D: int
+    max_blocks: int
+    max_seqlen_q: int
+    scale: float
+    dtype: str
+    layout: str
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+
+def paged_prefill_inputs(ctx_lens: list, q_lens: list, Hq: int, Hkv: int, D: int, *, seed: int,
+                         block_size: int = 16, tail: str = "zero", dtype: str = "bf16",
+                         scale: Optional[float] = None,
+                         layout: str = "rowmajor") -> PagedPrefillInputs:
+    """Chunked prefill over a paged cache: sequence n has ctx_lens[n] earlier
+    tokens and a new chunk of q_lens[n] tokens, all Sk = ctx + q of them in
+    the pool.  Draw order: the packed queries [total_q, Hq, D], then per
+    sequence its K then V ([Sk, Hkv, D]), then one permutation of the
+    physical blocks (logical blocks numbered sequence-major)."""
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    N = len(ctx)
+    sk = ctx + ql
+    cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), Hq, D), dtype=np.float32)
+    nblk = [(int(L) + block_size - 1) // block_size for L in sk]
+    NB = max(1, int(sum(nblk)))
+    max_blocks = max(1, max(nblk))
+    fill = np.nan if tail == "nan" else 0.0
+    kp = np.full((NB, Hkv, block_size, D), fill, dtype=np.float32)
+    vp = np.full((NB, Hkv, block_size, D), fill, dtype=np.float32)
+    logical = []
+    for n in range(N):
+        L = int(sk[n])
+        logical.append((rng.standard_normal((L, Hkv, D), dtype=np.float32),
+                        rng.standard_normal((L, Hkv, D), dtype=np.float32)))
+    perm = rng.permutation(NB)
+    table = np.full((N, max_blocks), -1, dtype=np.int32)
+    base = 0
+    for n in range(N):
+        L = int(sk[n])
+        for j in range(nblk[n]):
+            p = int(perm[base + j])
+            table[n, j] = p
+            t0, t1 = j * block_size, min(L, (j + 1) * block_size)
+            kp[p, :, : t1 - t0, :] = logical[n][0][t0:t1].transpose(1, 0, 2)
+            vp[p, :, : t1 - t0, :] = logical[n][1][t0:t1].transpose(1, 0, 2)
+        base += nblk[n]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kp, vp = _to_layout(kp, vp, layout, block_size, D)
+    return PagedPrefillInputs(
+        q=to_dtype(q, dtype), cu_seqlens_q=torch.from_numpy(cu), k_pool=to_dtype(kp, dtype),
+        v_pool=to_dtype(vp, dtype), block_table=torch.from_numpy(table),
+        seq_lens_k=torch.from_numpy(sk.astype(np.int32)), block_size=block_size, N=N, Hq=Hq,
+        Hkv=Hkv, D=D, max_blocks=max_blocks, max_seqlen_q=int(ql.max()) if N else 0,
+        scale=float(scale), dtype=dtype, layout=layout)
 
 
 def unshared_copy(d: DecodeInputs) -> DecodeInputs:
