@@ -23,7 +23,8 @@ __all__ = [
     "AttnError", "lib_path", "load", "attn_status_string", "attn_arch_supported",
     "attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
     "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_paged_blockskip",
-    "prefill", "prefill_blockskip", "decode_paged", "decode_paged_blockskip",
+    "attn_prefill_paged",
+    "prefill", "prefill_blockskip", "decode_paged", "decode_paged_blockskip", "prefill_paged",
 ]
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -68,6 +69,9 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged.restype = _I
     lib.attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                       _F, _P, ctypes.c_size_t, _P]
+    lib.attn_prefill_paged.restype = _I
+    lib.attn_prefill_paged.argtypes = [_P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I,
+                                       _I, _I, _I, _F, _P]
     lib.attn_decode_paged_blockskip.restype = _I
     lib.attn_decode_paged_blockskip.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I,
                                                 _I, _I, _I, _F, _F, _P, _P, _P, ctypes.c_size_t,
@@ -244,6 +248,34 @@ def attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_
     _check(st, "attn_decode_paged_blockskip")
 
 
+def attn_prefill_paged(q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse,
+                       max_seqlen_q: int, scale: float, block_size: int = 16, stream=None,
+                       layout: str = "rowmajor") -> None:
+    """Chunked / variable-length causal prefill over the paged cache into
+    caller-allocated o [total_q, Hq, D] and lse [total_q, Hq] (or None)."""
+    total_q, Hq, D = q.shape
+    N = int(seq_lens_k.shape[0])
+    NB, Hkv = k_pool.shape[0], k_pool.shape[1]
+    _dev(q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse)
+    if layout not in KV_LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
+    ks, vs = _pool_shapes(NB, Hkv, block_size, D, layout)
+    if tuple(k_pool.shape) != ks or tuple(v_pool.shape) != vs or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    for t in (cu_seqlens_q, block_table, seq_lens_k):
+        if t.dtype != torch.int32:
+            raise TypeError("cu_seqlens_q, block_table and seq_lens_k must be int32")
+    if cu_seqlens_q.shape != (N + 1,) or block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("cu_seqlens_q must be [N+1], block_table [N, max_blocks]")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (total_q, Hq)):
+        raise ValueError("lse must be float32 [total_q, Hq]")
+    st = load().attn_prefill_paged(
+        _ptr(q), _ptr(cu_seqlens_q), total_q, int(max_seqlen_q), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), _ptr(seq_lens_k), int(block_size), KV_LAYOUTS[layout], _ptr(o),
+        _ptr(lse), N, Hq, Hkv, D, NB, int(block_table.shape[1]), float(scale), _stream(stream))
+    _check(st, "attn_prefill_paged")
+
+
 # ------------------------------------------------------ allocating wrappers
 
 def prefill(q, k, v, causal: bool = True, scale: Optional[float] = None,
@@ -311,3 +343,17 @@ def decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, lam: float,
     attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse,
                                 scale, lam, workspace, bm, cnt, layout="mfma")
     return o, lse, bm, cnt
+
+
+def prefill_paged(q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, max_seqlen_q: int,
+                  scale: Optional[float] = None, block_size: int = 16):
+    """Allocate O and LSE and run the chunked prefill over a row-major paged
+    cache.  Returns (o [total_q, Hq, D], lse [total_q, Hq])."""
+    total_q, Hq, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    attn_prefill_paged(q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse,
+                       max_seqlen_q, scale, block_size)
+    return o, lse

@@ -197,4 +197,29 @@ int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v
                        workspace_bytes, 1, lambda, skip_bitmap, skipped_blocks, stream);
 }
 
+int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_seqlen_q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_table,
+                       const int32_t* seq_lens_k, int block_size, int kv_layout, void* o,
+                       float* lse, int num_seqs, int Hq, int Hkv, int D, int num_blocks,
+                       int max_blocks_per_seq, float scale, hipStream_t stream) {
+  if (!q || !cu_seqlens_q || !k_pool || !v_pool || !block_table || !seq_lens_k || !o)
+    return ATTN_ERR_INVALID_ARG;
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks_per_seq < 1 ||
+      total_q < 1 || max_seqlen_q < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!finite_pos(scale)) return ATTN_ERR_INVALID_ARG;
+  if (kv_layout != ATTN_KV_ROWMAJOR && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_INVALID_ARG;
+  if (kv_layout != ATTN_KV_ROWMAJOR) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != 16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * 16 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::PagedPrefillArgs a{q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse,
+                           num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, max_seqlen_q,
+                           scale};
+  return hip_status(attn::launch_prefill_paged(a, stream));
+}
+
 }  // extern "C"

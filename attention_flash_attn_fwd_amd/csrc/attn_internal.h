@@ -27,6 +27,22 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+
+// Chunked / variable-length causal prefill over a paged (row-major) cache.
+struct PagedPrefillArgs {
+  const void* q;              // bf16 [total_q, Hq, D]
+  const int32_t* cu_q;        // [N + 1]
+  const void* k_pool;         // bf16 [num_blocks, Hkv, 16, D]
+  const void* v_pool;
+  const int32_t* block_table; // [N, max_blocks]
+  const int32_t* seq_lens_k;  // [N]
+  void* o;                    // bf16 [total_q, Hq, D]
+  float* lse;                 // [total_q, Hq] or null
+  int N, Hq, Hkv, D, num_blocks, max_blocks, max_seqlen_q;
+  float scale;
+};
+
+hipError_t launch_prefill_paged(const PagedPrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {

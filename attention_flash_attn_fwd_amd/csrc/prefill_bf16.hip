@@ -68,6 +68,11 @@ struct Params {
   uint8_t* skip_map;
   unsigned long long* skip_count;
   int nT;
+  // chunked prefill over a paged cache (PAGED only)
+  const int32_t* cu_q;     // [N + 1] query offsets into the packed q / o / lse
+  const int32_t* seq_k;    // [N] cached tokens per sequence (Sk)
+  const int32_t* table;    // [N, max_blocks] block table
+  int N, max_blocks, num_blocks;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -101,6 +106,14 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                ::"v"(voff), "s"(gbase), "s"(m) : "memory");
+}
+
+// The same copy from a full per-lane 64-bit address (a tile gathered from
+// several pool blocks has no common scalar base).
+__device__ __forceinline__ void dma16_va(const void* addr, uint32_t lds_addr) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(addr), "s"(m) : "memory");
 }
 
 template <int N>
@@ -143,7 +156,7 @@ struct Tile {
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D, bool CAUSAL, bool SKIP>
+template <int D, bool CAUSAL, bool SKIP, bool PAGED>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   using T = Tile<D>;
   constexpr int NKS = D / 16;  // 16-dim k-steps of Q.K^T
@@ -157,10 +170,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
 
-  // ---- work item: heaviest query blocks first
+  // ---- work item: heaviest query blocks first (paged: across sequences)
   const int bid = blockIdx.x;
-  const int qblk = p.n_qblk - 1 - bid / p.n_hgrp;
   const int hg = bid % p.n_hgrp;
+  const int seq = PAGED ? (bid / p.n_hgrp) % p.N : 0;
+  const int qblk = p.n_qblk - 1 - (PAGED ? bid / p.n_hgrp / p.N : bid / p.n_hgrp);
   const int sub = hg % p.sub_per_kv;
   const int bk = hg / p.sub_per_kv;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
@@ -169,14 +183,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   // slots: equal causal tile counts keep both busy to the end.
   const int slot = SKIP ? wave : ((wave & 3) << 1) | (wave >> 2);
   const int head = kvh * p.G + sub * p.gw + (slot % p.gw);
-  const int S = p.S;
   const int row0 = qblk * p.rows_per_wg;
   const int q0 = row0 + (slot / p.gw) * 32;
+  // Sq query rows at key positions off .. off+Sq-1 of Sk keys (dense: all S)
+  int Sq = p.S, Sk = p.S, off = 0, qstart = 0;
+  if constexpr (PAGED) {
+    qstart = p.cu_q[seq];
+    Sq = p.cu_q[seq + 1] - qstart;
+    Sk = p.seq_k[seq];
+    off = Sk - Sq;
+    if (row0 >= Sq) return;  // whole workgroup past this chunk
+    if (Sq < 0 || off < 0 || Sk > p.max_blocks * 16) {
+      // lengths that do not fit the table: NaN rows, nothing read
+      const int row = q0 + n;
+      if (row < Sq) {
+        uint16_t* orow = p.o + ((size_t)(qstart + row) * p.Hq + head) * D;
+        for (int d = hf * 4; d < D; d += 8)
+          *reinterpret_cast<u32x2*>(orow + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+        if (hf == 0 && p.lse) p.lse[(size_t)(qstart + row) * p.Hq + head] = NAN;
+      }
+      return;
+    }
+  }
+  const int S = Sk;  // key count
 
-  const int wg_last = min(S, row0 + p.rows_per_wg) - 1;
-  const int n_tiles = CAUSAL ? wg_last / BN + 1 : (S + BN - 1) / BN;
-  const bool has_rows = q0 < S;
-  const int wave_tiles = !has_rows ? 0 : (CAUSAL ? min(S - 1, q0 + 31) / BN + 1 : n_tiles);
+  const int wg_last = min(Sq, row0 + p.rows_per_wg) - 1;
+  const int n_tiles = CAUSAL ? (off + wg_last) / BN + 1 : (S + BN - 1) / BN;
+  const bool has_rows = q0 < Sq;
+  const int wave_tiles = !has_rows ? 0 : (CAUSAL ? (off + min(Sq - 1, q0 + 31)) / BN + 1 : n_tiles);
 
   const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
   const uint16_t* Kg = p.k + kvbase;
@@ -209,6 +243,39 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     const uint32_t st = smem_base + (t % T::NST) * T::STAGE;
     const int key0 = t * BN;
     const bool ragged = key0 + BN > S;  // clamp keys past the end to the last key
+    if constexpr (PAGED) {
+      // the tile's 4 pool blocks (table entries clamped into the pool)
+      const int32_t* trow = p.table + (size_t)seq * p.max_blocks;
+      const int nbs = (S + 15) >> 4;
+      int e[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int idx = t * 4 + x;
+        const int v = idx < nbs ? trow[idx] : 0;
+        e[x] = min(max(v, 0), p.num_blocks - 1);
+      }
+      const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k);
+      const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v);
+      auto src = [&](const unsigned char* pool, int r, uint32_t choff) {
+        const int key = key0 + min(r, S - 1 - key0);
+        const int bl = (key >> 4) - t * 4;
+        const int ph = bl == 0 ? e[0] : bl == 1 ? e[1] : bl == 2 ? e[2] : e[3];
+        return pool + ((((size_t)ph * p.Hkv + kvh) << 4) + (key & 15)) * T::RB + choff;
+      };
+#pragma unroll
+      for (int j = 0; j < NJK; ++j) {
+        const int i = wave + j * kWaves;
+        if (i >= T::KSL) break;
+        dma16_va(src(kpool, krow[j], koff[j]), st + i * 1024);
+      }
+#pragma unroll
+      for (int j = 0; j < NJV; ++j) {
+        const int i = wave + j * kWaves;
+        if (i >= T::VSL) break;
+        dma16_va(src(vpool, vrow[j], voff[j]), st + T::KT + i * 1024);
+      }
+      return;
+    }
     const uint16_t* kb_ = Kg + (size_t)key0 * D;
     const uint16_t* vb_ = Vg + (size_t)key0 * D;
 #pragma unroll
@@ -239,11 +306,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   };
 
   // ---- Q fragment (B operand): query q0+n, dims ks*16 + hf*8 .. +7
-  const size_t qbase = ((size_t)b * p.Hq + head) * S;
+  const size_t qbase = ((size_t)b * p.Hq + head) * Sq;
+  // element offset of query row r (dense [B,Hq,S,D]; paged packed [total_q,Hq,D])
+  auto qrow_off = [&](int r) -> size_t {
+    return PAGED ? ((size_t)(qstart + r) * p.Hq + head) * D : (qbase + r) * D;
+  };
   bf16x8 qf[NKS];
   {
-    const int qrow = min(q0 + n, S - 1);
-    const uint16_t* qp = p.q + (qbase + qrow) * D + hf * 8;
+    const int qrow = min(q0 + n, Sq - 1);
+    const uint16_t* qp = p.q + qrow_off(qrow) + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
@@ -270,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   float l = 0.f;
   unsigned skipped = 0;
   const float sl2 = p.sl2;
-  const int first_masked = CAUSAL ? min(q0 / BN, S / BN) : S / BN;
+  const int first_masked = CAUSAL ? min((off + q0) / BN, S / BN) : S / BN;
 
   // S^T of key tile t (raw scores) = K Q^T: two independent 32-key
   // accumulator chains, operand reads running ahead of the MFMAs
@@ -303,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = c0 + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          if (key >= S || (CAUSAL && key > qi)) sc[kb][i] = -INFINITY;
+          if (key >= S || (CAUSAL && key > off + qi)) sc[kb][i] = -INFINITY;
         }
     }
     float m0 = fmaxf(sc[0][0], sc[1][0]), m1 = fmaxf(sc[0][1], sc[1][1]);
@@ -472,9 +543,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   if (!has_rows) return;
   const float lt = half_swap_add(l);
   const int row = q0 + n;
-  if (row >= S) return;
+  if (row >= Sq) return;
   const float inv = 1.f / lt;
-  uint16_t* orow = p.o + (qbase + row) * D;
+  uint16_t* orow = p.o + qrow_off(row);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -484,12 +555,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
                  pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
       *reinterpret_cast<u32x2*>(orow + d0) = w;
     }
-  if (hf == 0 && p.lse) p.lse[qbase + row] = (m_used + __log2f(lt)) * kLn2;
+  if (hf == 0 && p.lse)
+    p.lse[PAGED ? (size_t)(qstart + row) * p.Hq + head : qbase + row] = (m_used + __log2f(lt)) * kLn2;
 }
 
-template <int D, bool CAUSAL, bool SKIP>
+template <int D, bool CAUSAL, bool SKIP, bool PAGED = false>
 hipError_t launch_one(const Params& p, int grid, hipStream_t stream) {
-  auto kern = prefill_bf16_kernel<D, CAUSAL, SKIP>;
+  auto kern = prefill_bf16_kernel<D, CAUSAL, SKIP, PAGED>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -541,6 +613,38 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   }
   return a.D == 64 ? launch_one<64, false, false>(p, g, stream)
                    : launch_one<128, false, false>(p, g, stream);
+}
+
+hipError_t launch_prefill_paged(const PagedPrefillArgs& a, hipStream_t stream) {
+  Params p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k_pool);
+  p.v = static_cast<const uint16_t*>(a.v_pool);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.lse = a.lse;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.S = 0;
+  p.G = a.Hq / a.Hkv;
+  int gw = 8;
+  while (p.G % gw) gw >>= 1;
+  p.gw = gw;
+  p.rows_per_wg = 32 * kWaves / gw;
+  p.n_qblk = (a.max_seqlen_q + p.rows_per_wg - 1) / p.rows_per_wg;
+  p.sub_per_kv = p.G / gw;
+  p.n_hgrp = a.Hkv * p.sub_per_kv;
+  p.sl2 = a.scale * 1.4426950408889634f;
+  p.cu_q = a.cu_q;
+  p.seq_k = a.seq_lens_k;
+  p.table = a.block_table;
+  p.N = a.N;
+  p.max_blocks = a.max_blocks;
+  p.num_blocks = a.num_blocks;
+  const long long grid = (long long)p.n_qblk * a.N * p.n_hgrp;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int g = (int)grid;
+  return a.D == 64 ? launch_one<64, true, false, true>(p, g, stream)
+                   : launch_one<128, true, false, true>(p, g, stream);
 }
 
 }  // namespace attn

@@ -80,8 +80,8 @@ def main():
     import torch
 
     import attention_flash_attn_fwd_amd as A
-    from workloads import (CONFIGS, blockskip_inputs, decode_inputs, prefill_flops, prefill_inputs,
-                           shared_prefix_decode_inputs)
+    from workloads import (CONFIGS, blockskip_inputs, decode_inputs, paged_prefill_inputs,
+                           prefill_flops, prefill_inputs, shared_prefix_decode_inputs)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -257,6 +257,25 @@ def main():
                 "logical_kv_GBps": round(kvb / mk / 1e9, 1),
                 "read_kv_GBps": round(kvb * (1 - 0.5 * frac) / mk / 1e9, 1)}
             del bpools
+
+        # chunked prefill over the paged cache: 8 sequences with 3584 cached
+        # tokens and a new 512-token chunk each (GQA 32/8, D=128, row-major pools)
+        ctx_l, q_l = [3584] * 8, [512] * 8
+        wc = paged_prefill_inputs(ctx_l, q_l, cd["Hq"], cd["Hkv"], cd["D"], seed=2005)
+        cq, ccu = wc.q.to(dev), wc.cu_seqlens_q.to(dev)
+        ckp, cvp = wc.k_pool.to(dev), wc.v_pool.to(dev)
+        cbt, csk = wc.block_table.to(dev), wc.seq_lens_k.to(dev)
+        co = torch.empty_like(cq)
+        clse = torch.empty((wc.total_q, cd["Hq"]), dtype=torch.float32, device=dev)
+        mc = time_it(lambda: A.attn_prefill_paged(cq, ccu, ckp, cvp, cbt, csk, co, clse,
+                                                  wc.max_seqlen_q, wc.scale), 10)
+        pairs = sum(qn * c + qn * (qn + 1) // 2 for c, qn in zip(ctx_l, q_l))
+        fc = 4 * cd["Hq"] * cd["D"] * pairs
+        secondary["chunked_prefill_paged"] = {
+            "TFLOPs": round(fc / mc / 1e12, 1), "frac_mfma_peak": round(fc / mc / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "us_per_launch": round(mc * 1e6, 1), "flops": fc,
+            "note": "8 seqs x (3584 cached + 512 new) tokens, Hq=32 Hkv=8 D=128, bottom-right causal"}
+        del ckp, cvp
 
         c3 = CONFIGS["gqa_causal_s8192"]
         w3 = prefill_inputs(c3["B"], c3["Hq"], c3["Hkv"], c3["S"], c3["D"], seed=c3["seed"])

@@ -212,6 +212,31 @@ int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v
                                 unsigned long long* skipped_blocks, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* Chunked / variable-length causal prefill over the paged KV cache (the
+ * prefill-with-KV-cache case of "flash-attention与TensorRT-LLM集成" and the
+ * block table of "LLM推理优化技术综述", PageAttention part).  Sequence n
+ * has Sk = seq_lens_k[n] tokens whose K/V are already in the pools (earlier
+ * context and the new chunk); its Sq = cu_seqlens_q[n+1] - cu_seqlens_q[n]
+ * queries are its last Sq positions: query i sees the keys
+ * j <= Sk - Sq + i (causal, bottom-right aligned).
+ *   q, o          : bf16 [total_q, Hq, D], packed sequence after sequence
+ *   cu_seqlens_q  : int32 [num_seqs + 1], cu[0] = 0, cu[num_seqs] = total_q
+ *   max_seqlen_q  : an upper bound on every Sq (sizes the grid)
+ *   lse           : float32 [total_q, Hq] (natural log) or NULL
+ *   k_pool/v_pool : bf16, kv_layout must be ATTN_KV_ROWMAJOR
+ *                   ([num_blocks, Hkv, 16, D]; ATTN_ERR_UNSUPPORTED otherwise)
+ *   block_table   : int32 [num_seqs, max_blocks_per_seq]
+ * Requirements on the device data (not checked on the host): Sq <= Sk and
+ * Sk <= 16 * max_blocks_per_seq (a sequence breaking them gets NaN rows),
+ * Sq <= max_seqlen_q, valid table entries (out-of-range entries are
+ * clamped into the pool: the result is then unspecified, no read leaves
+ * the pool). */
+int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_seqlen_q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_table,
+                       const int32_t* seq_lens_k, int block_size, int kv_layout, void* o,
+                       float* lse, int num_seqs, int Hq, int Hkv, int D, int num_blocks,
+                       int max_blocks_per_seq, float scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def _declared():
 def test_header_lists_the_entry_points():
     names = _declared()
     for need in ("attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
-                 "attn_decode_paged", "attn_decode_paged_blockskip",
+                 "attn_decode_paged", "attn_decode_paged_blockskip", "attn_prefill_paged",
                  "attn_decode_workspace_bytes", "attn_status_string", "attn_arch_supported"):
         assert need in names
 
@@ -137,3 +137,24 @@ def test_decode_blockskip_validation_without_device():
     assert call(bt=None) == -1
     assert call(D=96) == -2
     assert call(ws=None) == -4
+
+
+def test_prefill_paged_validation_without_device():
+    lib = A.load()
+
+    def call(**kw):
+        a = dict(q=8, cu=8, tq=40, mq=20, kp=8, vp=8, bt=8, sk=8, bs=16, lay=0, o=8, N=2, Hq=8,
+                 Hkv=2, D=128, NB=8, MB=4, scale=0.1)
+        a.update(kw)
+        return lib.attn_prefill_paged(a["q"], a["cu"], a["tq"], a["mq"], a["kp"], a["vp"], a["bt"],
+                                      a["sk"], a["bs"], a["lay"], a["o"], None, a["N"], a["Hq"],
+                                      a["Hkv"], a["D"], a["NB"], a["MB"], a["scale"], None)
+    assert call(cu=None) == -1
+    assert call(tq=0) == -1
+    assert call(mq=0) == -1
+    assert call(Hq=6, Hkv=4) == -1
+    assert call(scale=-1.0) == -1
+    assert call(lay=5) == -1
+    assert call(lay=1) == -2           # MFMA-native pools: not supported here
+    assert call(bs=32) == -2
+    assert call(D=96) == -2

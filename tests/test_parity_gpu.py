@@ -16,9 +16,10 @@ import pytest
 import torch
 
 import attention_flash_attn_fwd_amd as A
-from oracle import ref_blockskip, ref_decode_paged, ref_decode_paged_blockskip, ref_prefill
-from workloads import (CONFIGS, blockskip_inputs, decode_inputs, prefill_inputs,
-                       shared_prefix_decode_inputs, unshared_copy, upcast_f64)
+from oracle import (ref_blockskip, ref_decode_paged, ref_decode_paged_blockskip, ref_prefill,
+                    ref_prefill_paged)
+from workloads import (CONFIGS, blockskip_inputs, decode_inputs, paged_prefill_inputs,
+                       prefill_inputs, shared_prefix_decode_inputs, unshared_copy, upcast_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -204,6 +205,54 @@ def test_paged_decode_shared_prefix(layout):
     # the same logical cache without sharing gives the identical bits
     o2, l2 = _run_decode(unshared_copy(d))
     assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+# ------------------------------------------------------- chunked paged prefill
+
+def _run_prefill_paged(d):
+    o, lse = A.prefill_paged(d.q.cuda(), d.cu_seqlens_q.cuda(), d.k_pool.cuda(), d.v_pool.cuda(),
+                             d.block_table.cuda(), d.seq_lens_k.cuda(), d.max_seqlen_q,
+                             scale=d.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 128), (16, 2, 64), (8, 1, 128)])
+def test_prefill_paged_varlen(Hq, Hkv, D):
+    ctx = [0, 37, 1000, 5, 300, 0, 64]
+    ql = [200, 1, 300, 600, 63, 1, 257]
+    say(f"chunked paged prefill Hq{Hq} Hkv{Hkv} D{D} ctx={ctx} q={ql}")
+    d = paged_prefill_inputs(ctx, ql, Hq, Hkv, D, seed=120 + D + Hq, tail="nan")
+    o, lse = _run_prefill_paged(d)
+    ro, rl = ref_prefill_paged(upcast_f64(d.q), d.cu_seqlens_q.numpy(), upcast_f64(d.k_pool),
+                               upcast_f64(d.v_pool), d.block_table.numpy(),
+                               d.seq_lens_k.numpy(), 16, d.scale)
+    _compare(o, lse, ro, rl, TOL["bf16"], "paged prefill")
+
+
+def test_prefill_paged_two_chunks_match_dense_prefill():
+    say("two chunks of one sequence through the paged cache = the dense causal prefill")
+    S, Hq, Hkv, D = 700, 8, 2, 128
+    w = prefill_inputs(1, Hq, Hkv, S, D, seed=131)
+    od, ld = _run_prefill(w)                               # [1, Hq, S, D]
+    # the same K/V in a paged pool (blocks in order), queries split at 300
+    nb = (S + 15) // 16
+    kp = torch.zeros((nb, Hkv, 16, D), dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    for j in range(nb):
+        t0, t1 = j * 16, min(S, (j + 1) * 16)
+        kp[j, :, : t1 - t0] = w.k[0, :, t0:t1]
+        vp[j, :, : t1 - t0] = w.v[0, :, t0:t1]
+    table = torch.arange(nb, dtype=torch.int32).repeat(2, 1)
+    qp = w.q[0].permute(1, 0, 2).contiguous()              # [S, Hq, D]
+    cu = torch.tensor([0, 300, 700], dtype=torch.int32)
+    seq_k = torch.tensor([300, 700], dtype=torch.int32)    # chunk 1 sees its own 300 keys
+    o, lse = A.prefill_paged(qp.cuda(), cu.cuda(), kp.cuda(), vp.cuda(), table.cuda(),
+                             seq_k.cuda(), 400, scale=w.scale)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().transpose(1, 0, 2)[None]
+    lse = lse.cpu().numpy().T[None]
+    _compare(o, lse, od.astype(np.float64), ld.astype(np.float64), TOL["bf16"], "chunks vs dense")
 
 
 # ---------------------------------------------------------- decode block skip
