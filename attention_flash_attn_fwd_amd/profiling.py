@@ -28,7 +28,7 @@ CSRC = os.path.join(ROOT, "attention_flash_attn_fwd_amd", "csrc")
 
 # kernel-name fragment -> (record key, source file whose hash the record carries)
 TRACKED = {
-    "prefill_bf16_kernel<128, true, false>": ("prefill_bf16", "prefill_bf16.hip"),
+    "prefill_bf16_kernel<128, true, false, false>": ("prefill_bf16", "prefill_bf16.hip"),
     "decode_native_kernel<128>": ("decode_native", "decode_paged.hip"),
     "decode_split_kernel<128>": ("decode_split", "decode_paged.hip"),
     "decode_merge_kernel<128>": ("decode_merge", "decode_paged.hip"),
