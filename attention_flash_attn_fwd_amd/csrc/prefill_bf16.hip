@@ -147,10 +147,6 @@ struct Tile {
   static constexpr int STAGE = KT + VT;
   static constexpr int NST = 4;               // LDS stages: t-1 (role B), t, t+1, t+2 in flight
   static constexpr size_t lds_bytes = (size_t)NST * STAGE;
-  // DMA blocks issued by wave w per tile: blocks w, w+8, ... of KSL + VSL
-  static __device__ __forceinline__ int dma_count(int w) {
-    return (KSL - w + kWaves - 1) / kWaves + (VSL - w + kWaves - 1) / kWaves;
-  }
 };
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -218,26 +214,28 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
 
   // ---- asynchronous global -> LDS copy of tile t into stage t % NST.
   // One wave-wide load fills 1 KiB of LDS (16 bytes per lane, in lane
-  // order); the lane fetches the global chunk that the swizzle puts there.
-  // Keys past the end are clamped to the last key and masked later.
-  // Per-lane source offsets of this wave's DMA blocks within a tile: block
-  // i covers LDS slots 64i .. 64i+63, slot g = row g / SL, chunk g % SL (a
-  // pad slot re-reads chunk 0 of its row).  Fixed for every tile; the tile's
-  // first key enters through the scalar base address.
-  constexpr int NJK = (T::KSL + kWaves - 1) / kWaves, NJV = (T::VSL + kWaves - 1) / kWaves;
-  uint32_t koff[NJK], voff[NJV];
-  int krow[NJK], vrow[NJV];
+  // order); the lane fetches the global chunk that the padded layout puts
+  // there.  The NBLK blocks of a stage (K blocks 0 .. KSL-1, then V blocks)
+  // are numbered jointly and dealt round robin, block w + 8j to wave w, so
+  // every wave issues DMA_LO or DMA_HI of them; since the K tile is exactly
+  // KSL KiB, block i always lands at byte i KiB of the stage.  Slot g of a
+  // block is row g / SL, chunk g % SL (a pad slot re-reads chunk 0 of its
+  // row).  The per-lane source offsets are fixed for every tile: the tile's
+  // first key enters through the scalar base address.  Keys past the end
+  // are clamped to the last key and masked later.
+  constexpr int NBLK = T::KSL + T::VSL;
+  constexpr int DMA_HI = (NBLK + kWaves - 1) / kWaves, DMA_LO = NBLK / kWaves;
+  const bool dma_hi = wave < NBLK % kWaves;
+  uint32_t doff[DMA_HI];  // row * RB + chunk offset
+  int drow[DMA_HI];
 #pragma unroll
-  for (int j = 0; j < NJK; ++j) {
-    const int g = (wave + j * kWaves) * 64 + lane, c = g % T::KSL;
-    krow[j] = g / T::KSL;
-    koff[j] = (c < T::CH ? c : 0) * 16;
-  }
-#pragma unroll
-  for (int j = 0; j < NJV; ++j) {
-    const int g = (wave + j * kWaves) * 64 + lane, c = g % T::VSL;
-    vrow[j] = g / T::VSL;
-    voff[j] = (c < T::CH ? c : 0) * 16;
+  for (int j = 0; j < DMA_HI; ++j) {
+    const int i = wave + j * kWaves;
+    const bool is_k = i < T::KSL;
+    const int sl = is_k ? T::KSL : T::VSL;
+    const int g = (is_k ? i : i - T::KSL) * 64 + lane, c = g % sl;
+    drow[j] = g / sl;
+    doff[j] = (uint32_t)drow[j] * T::RB + (c < T::CH ? c : 0) * 16;
   }
   auto issue = [&](int t) {
     const uint32_t st = smem_base + (t % T::NST) * T::STAGE;
@@ -256,53 +254,44 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
       }
       const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k);
       const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v);
-      auto src = [&](const unsigned char* pool, int r, uint32_t choff) {
+#pragma unroll
+      for (int j = 0; j < DMA_HI; ++j) {
+        const int i = wave + j * kWaves;
+        if (j == DMA_LO && !dma_hi) break;
+        const int r = drow[j];
         const int key = key0 + min(r, S - 1 - key0);
         const int bl = (key >> 4) - t * 4;
         const int ph = bl == 0 ? e[0] : bl == 1 ? e[1] : bl == 2 ? e[2] : e[3];
-        return pool + ((((size_t)ph * p.Hkv + kvh) << 4) + (key & 15)) * T::RB + choff;
-      };
-#pragma unroll
-      for (int j = 0; j < NJK; ++j) {
-        const int i = wave + j * kWaves;
-        if (i >= T::KSL) break;
-        dma16_va(src(kpool, krow[j], koff[j]), st + i * 1024);
-      }
-#pragma unroll
-      for (int j = 0; j < NJV; ++j) {
-        const int i = wave + j * kWaves;
-        if (i >= T::VSL) break;
-        dma16_va(src(vpool, vrow[j], voff[j]), st + T::KT + i * 1024);
+        const uint32_t choff = doff[j] - (uint32_t)r * T::RB;
+        const unsigned char* pool = i < T::KSL ? kpool : vpool;
+        dma16_va(pool + ((((size_t)ph * p.Hkv + kvh) << 4) + (key & 15)) * T::RB + choff,
+                 st + i * 1024);
       }
       return;
     }
     const uint16_t* kb_ = Kg + (size_t)key0 * D;
     const uint16_t* vb_ = Vg + (size_t)key0 * D;
+    if (!ragged) {
 #pragma unroll
-    for (int j = 0; j < NJK; ++j) {
-      const int i = wave + j * kWaves;
-      if (i >= T::KSL) break;
-      const int r = ragged ? min(krow[j], S - 1 - key0) : krow[j];
-      dma16(kb_, (uint32_t)r * T::RB + koff[j], st + i * 1024);
-    }
+      for (int j = 0; j < DMA_HI; ++j) {
+        const int i = wave + j * kWaves;
+        if (j == DMA_LO && !dma_hi) break;
+        dma16(i < T::KSL ? kb_ : vb_, doff[j], st + i * 1024);
+      }
+    } else {
+      const int lim = S - 1 - key0;
 #pragma unroll
-    for (int j = 0; j < NJV; ++j) {
-      const int i = wave + j * kWaves;
-      if (i >= T::VSL) break;
-      const int r = ragged ? min(vrow[j], S - 1 - key0) : vrow[j];
-      dma16(vb_, (uint32_t)r * T::RB + voff[j], st + T::KT + i * 1024);
+      for (int j = 0; j < DMA_HI; ++j) {
+        const int i = wave + j * kWaves;
+        if (j == DMA_LO && !dma_hi) break;
+        const uint32_t o = doff[j] - (uint32_t)(drow[j] - min(drow[j], lim)) * T::RB;
+        dma16(i < T::KSL ? kb_ : vb_, o, st + i * 1024);
+      }
     }
   };
-  const int n_dma = T::dma_count(wave);
   // wait until only the DMA blocks of the newest tile are in flight
   auto wait_all_but_newest = [&]() {
-    switch (n_dma) {
-      case 2: wait_vmem<2>(); break;
-      case 3: wait_vmem<3>(); break;
-      case 4: wait_vmem<4>(); break;
-      case 5: wait_vmem<5>(); break;
-      default: wait_vmem<6>(); break;
-    }
+    if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO>(); else wait_vmem<DMA_HI>();
   };
 
   // ---- Q fragment (B operand): query q0+n, dims ks*16 + hf*8 .. +7
@@ -366,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // mask (diagonal and ragged tiles only) and scaled row max of a score tile
-  auto row_max = [&](int t, f32x16* sc) -> float {
+  auto mask_tile = [&](int t, f32x16* sc) {
     if (t >= first_masked) {
       const int c0 = t * BN, qi = q0 + n;
 #pragma unroll
@@ -377,6 +366,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
           if (key >= S || (CAUSAL && key > off + qi)) sc[kb][i] = -INFINITY;
         }
     }
+  };
+  auto tile_max = [&](const f32x16* sc) -> float {
     float m0 = fmaxf(sc[0][0], sc[1][0]), m1 = fmaxf(sc[0][1], sc[1][1]);
 #pragma unroll
     for (int i = 2; i < 16; i += 2) {
@@ -384,6 +375,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
       m1 = fmaxf(fmaxf(m1, sc[0][i + 1]), sc[1][i + 1]);
     }
     return half_swap_max(fmaxf(m0, m1)) * sl2;
+  };
+  auto row_max = [&](int t, f32x16* sc) -> float {
+    mask_tile(t, sc);
+    return tile_max(sc);
   };
   // softmax of a score tile into bf16 P (packed for the P.V MFMA).  The
   // exponent reference moves (with a rescale of O and l) only when the row
@@ -487,30 +482,44 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     // 1 its share of tile j+3 (and of tile 2 in its extra first slot); the
     // issue stalls the issuing wave, and an MFMA-phase wave would hold the
     // matrix core idle meanwhile.  The stage a share overwrites was last
-    // read before the preceding barrier.  Before the barrier that precedes
-    // the first Q.K^T of tile j+1, every wave waits until only its newest
-    // share (tile j+2) is in flight.
+    // read before the preceding barrier.  At the end of its VALU phase j
+    // every wave waits until only the share it has just issued is in
+    // flight: group 0's share of tile j+1 is then complete at the barrier
+    // after which the first Q.K^T of tile j+1 starts, group 1's share of
+    // tile j+2 a half iteration before the corresponding barrier.
+    //
+    // The iterations in which every step is present (no causal mask, no
+    // pipeline start or end) run a copy of the body without the tests.
     const int grp = wave >> 2;
     uint32_t pk[2][8];
-    auto wait_tail = [&](int j) {
-      if (j + 2 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
-    };
-    if (n_tiles > 1) wait_all_but_newest(); else wait_vmem<0>();
     block_barrier();
     if (grp == 1) {
       if (2 < n_tiles) issue(2);
       block_barrier();
     }
-    for (int j = 0; j <= n_tiles; ++j) {
+    auto general = [&](int j) {
       if (j >= 1 && j - 1 < wave_tiles) pv(j - 1, pk);
       if (j < wave_tiles) qk(j, sc);
-      if (grp == 1) wait_tail(j);
       block_barrier();
-      if (j + 2 + grp < n_tiles) issue(j + 2 + grp);
+      const bool issues = j + 2 + grp < n_tiles;
+      if (issues) issue(j + 2 + grp);
       if (j < wave_tiles) softmax(sc, row_max(j, sc), pk);
-      if (grp == 0) wait_tail(j);
+      if (issues) wait_all_but_newest(); else wait_vmem<0>();
+      block_barrier();
+    };
+    general(0);
+    const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
+    int j = 1;
+    for (; j < j_ss; ++j) {
+      pv(j - 1, pk);
+      qk(j, sc);
+      block_barrier();
+      issue(j + 2 + grp);
+      softmax(sc, tile_max(sc), pk);
+      wait_all_but_newest();
       block_barrier();
     }
+    for (; j <= n_tiles; ++j) general(j);
     if (grp == 0) block_barrier();
   } else {
     // Block skip: the decision on a 64-row tile needs the row maxima of both
