@@ -16,4 +16,7 @@ from .attention import (  # noqa: F401
     pool_rows,
     ref_decode_paged_blockskip,
     ref_prefill_paged,
+    fp8_e4m3_value,
+    fp8_pool_rows,
+    ref_decode_paged_fp8,
 )

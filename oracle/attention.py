@@ -34,7 +34,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * decode: the single new query sees all L cached tokens (no mask);
   * block skip: whole T x T tiles per query head, ascending key-tile order,
     strict test (tile row max) - (running max) < ln(lambda), a tile skipped
-    only when every one of its rows passes the test.
+    only when every one of its rows passes the test;
+  * FP8 KV cache: E4M3 codes (the "FN" variant: no infinities, S.1111.111 is
+    NaN) with one fp32 scale per pool, cached value = scale * code value.
 """
 from __future__ import annotations
 
@@ -44,7 +46,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["kv_head_of", "ref_prefill", "ref_decode_paged", "ref_blockskip", "pool_rows",
-           "ref_decode_paged_blockskip", "ref_prefill_paged"]
+           "ref_decode_paged_blockskip", "ref_prefill_paged", "fp8_e4m3_value",
+           "fp8_pool_rows", "ref_decode_paged_fp8"]
 
 
 def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
@@ -351,3 +354,63 @@ def ref_prefill_paged(q: np.ndarray, cu_seqlens_q: np.ndarray, k_pool: np.ndarra
             out[r0:r1, h] = p @ vn
             lse[r0:r1, h] = l
     return out, lse
+
+
+def fp8_e4m3_value(code) -> np.ndarray:
+    """fp64 value of FP8 E4M3 codes.
+
+    FP8 with the E4M3 encoding is one of the low-precision formats the
+    TensorRT-LLM page lists ("TensorRT-LLM：大模型推理加速的工业级引擎",
+    六大核心优化技术 / 量化, and the 深入版解读 note on E4M3/E5M2).  The page
+    does not spell the encoding out; this is the common E4M3 "FN" format:
+    bit 7 sign, bits 6..3 exponent e with bias 7, bits 2..0 mantissa m.
+      e = 0:                  (-1)^s * (m / 8) * 2^(1 - 7)   (subnormal)
+      0 < e, not (e = 15 and m = 7): (-1)^s * (1 + m / 8) * 2^(e - 7)
+      e = 15 and m = 7:       NaN (there are no infinities; largest finite 448)
+    """
+    c = np.asarray(code).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** (1 - 7), (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * mag
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+def fp8_pool_rows(pool: np.ndarray, which: str, D: int, block_size: int = 16) -> np.ndarray:
+    """Token rows [NB, Hkv, block_size, D] of an FP8 pool in the MFMA-native
+    byte order (one contiguous run of block_size * D bytes per (block, head)).
+
+    Inside a run, with c = d // 16:
+      K byte (t, d) at (c // 4) * 1024 + ((c % 4) * 16 + t) * 16 + d % 16
+      V byte (t, d) at (b // 4) * 1024 + ((t // 4) * 16 + d % 16) * 16
+                       + (b % 4) * 4 + t % 4,    b = d // 16
+    (block_size = 16).  Returns the codes rearranged; a pure permutation."""
+    if block_size != 16 or D % 64:
+        raise ValueError("the FP8 pool layout needs block_size 16 and D % 64 == 0")
+    NB, Hkv = pool.shape[:2]
+    run = pool.reshape(NB, Hkv, block_size * D)
+    t = np.arange(block_size)[:, None]
+    d = np.arange(D)[None, :]
+    c = d // 16
+    if which == "k":
+        off = (c // 4) * 1024 + ((c % 4) * 16 + t) * 16 + d % 16
+    elif which == "v":
+        off = (c // 4) * 1024 + ((t // 4) * 16 + d % 16) * 16 + (c % 4) * 4 + t % 4
+    else:
+        raise ValueError(which)
+    return run[:, :, off]
+
+
+def ref_decode_paged_fp8(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                         block_table: np.ndarray, seq_lens: np.ndarray, block_size: int,
+                         scale: float, k_scale: float, v_scale: float):
+    """Decode attention over an FP8 paged KV cache [KV]: the codes are
+    decoded (:func:`fp8_e4m3_value`), multiplied by their pool's scale, and
+    the plain decode of :func:`ref_decode_paged` runs on those values.
+    k_pool / v_pool: uint8 codes [NB, Hkv, block_size * D] in the byte order
+    of :func:`fp8_pool_rows`."""
+    D = q.shape[-1]
+    k = k_scale * fp8_e4m3_value(fp8_pool_rows(k_pool, "k", D, block_size))
+    v = v_scale * fp8_e4m3_value(fp8_pool_rows(v_pool, "v", D, block_size))
+    return ref_decode_paged(q, k, v, block_table, seq_lens, block_size, scale)

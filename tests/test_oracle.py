@@ -543,3 +543,85 @@ def test_decode_layouts_hold_the_same_cache():
                           b.block_table.numpy(), b.seq_lens.numpy(), 16, b.scale, layout="mfma")
     np.testing.assert_array_equal(oa[0], ob[0])
     np.testing.assert_array_equal(oa[1], ob[1])
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache
+
+def test_fp8_code_values_match_torch_and_closed_forms():
+    """The E4M3 table written from the format definition equals torch's own
+    float8_e4m3fn decoding on all 256 codes (NaN where torch has NaN), and
+    hits the format's landmark values."""
+    from oracle import fp8_e4m3_value
+    v = fp8_e4m3_value(np.arange(256))
+    t = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(v, t)                      # NaNs compare equal here
+    assert v[0x38] == 1.0 and v[0x30] == 0.5 and v[0x3C] == 1.5
+    assert v[0x7E] == 448.0                                  # largest finite
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9  # subnormals
+    assert v[0x08] == 2.0 ** -6                              # smallest normal
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                           # codes 0..126 increase
+    np.testing.assert_array_equal(v[0x80:0xFF], -pos)         # sign bit
+
+
+def test_fp8_pool_byte_order_and_dequantized_decode():
+    """The oracle's reading of the FP8 pool byte order inverts the
+    generator's (written separately, as reshapes), a few bytes sit where the
+    layout definition puts them, and the FP8 decode equals the plain decode
+    on the pools dequantized by torch."""
+    from oracle import fp8_pool_rows, ref_decode_paged_fp8
+    from workloads import fp8_decode_inputs
+    f = fp8_decode_inputs(N=3, Hq=8, Hkv=2, D=128, seed=71, lens=[17, 1, 40], tail="nan")
+    b = f.base
+    kp, vp = f.k_pool.numpy(), f.v_pool.numpy()
+    kc, vc = f.k_codes.numpy(), f.v_codes.numpy()
+    np.testing.assert_array_equal(fp8_pool_rows(kp, "k", 128), kc)
+    np.testing.assert_array_equal(fp8_pool_rows(vp, "v", 128), vc)
+    # K (token 3, dim 5*16+2): chunk 5 -> run byte 1024 + (1*16 + 3)*16 + 2
+    assert kp[1, 1, 1024 + 19 * 16 + 2] == kc[1, 1, 3, 82]
+    # V (token 6, dim 6*16+9): group 1, block 6 -> 1024 + (1*16 + 9)*16 + 2*4 + 2
+    assert vp[2, 0, 1024 + 25 * 16 + 8 + 2] == vc[2, 0, 6, 105]
+    args = (b.block_table.numpy(), b.seq_lens.numpy(), 16, b.scale)
+    q = upcast_f64(b.q)
+    o, l = ref_decode_paged_fp8(q, kp, vp, *args, f.k_scale, f.v_scale)
+    o2, l2 = ref_decode_paged(q, f.k_rows.numpy(), f.v_rows.numpy(), *args)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+    assert np.isfinite(o).all()                               # NaN tail codes never read
+
+
+def test_fp8_decode_within_quantisation_bound():
+    """Against the plain decode on the unquantised bf16 pools, the FP8
+    decode stays inside the bound that E4M3 rounding allows: with
+    dV = max |v_hat - v| and E = scale * max_j sum_d |q_d| |k_hat_jd - k_jd|,
+    |O_hat - O| <= dV + (exp(2E) - 1) max |v_hat|  and  |LSE_hat - LSE| <= E.
+    A wrong scale, byte order or code value breaks it at once."""
+    from oracle import ref_decode_paged_fp8
+    from workloads import fp8_decode_inputs
+    f = fp8_decode_inputs(N=4, Hq=8, Hkv=2, D=64, seed=72, lmin=1, lmax=300)
+    b = f.base
+    q = upcast_f64(b.q)
+    table, lens = b.block_table.numpy(), b.seq_lens.numpy()
+    o, l = ref_decode_paged_fp8(q, f.k_pool.numpy(), f.v_pool.numpy(), table, lens, 16, b.scale,
+                                f.k_scale, f.v_scale)
+    k, v = upcast_f64(b.k_pool), upcast_f64(b.v_pool)
+    o_ref, l_ref = ref_decode_paged(q, k, v, table, lens, 16, b.scale)
+    kh, vh = f.k_rows.numpy(), f.v_rows.numpy()
+    # the E4M3 rounding itself: relative 2^-4 (normal), absolute 2^-10 * scale (subnormal)
+    assert np.all(np.abs(kh - k) <= np.maximum(2.0 ** -4 * np.abs(k), 2.0 ** -10 * f.k_scale) + 1e-15)
+    for n in range(b.N):
+        L = int(lens[n])
+        t = np.arange(L)
+        ph, sl = table[n, t // 16], t % 16
+        for h in range(b.Hq):
+            g = h // (b.Hq // b.Hkv)
+            dk = np.abs(kh[ph, g, sl] - k[ph, g, sl])          # [L, D]
+            dv = np.abs(vh[ph, g, sl] - v[ph, g, sl]).max()
+            E = b.scale * (dk @ np.abs(q[n, h])).max()
+            bound = dv + math.expm1(2 * E) * np.abs(vh[ph, g, sl]).max()
+            assert np.abs(o[n, h] - o_ref[n, h]).max() <= bound + 1e-12
+            assert abs(l[n, h] - l_ref[n, h]) <= E + 1e-12
+    # and the bound is not vacuous: the quantised result is close
+    assert np.abs(o - o_ref).max() < 0.25

@@ -27,6 +27,11 @@ Layouts:
       "rowmajor": k_pool, v_pool [NB, Hkv, block_size, D]
       "mfma":     k_pool [NB, Hkv, D/8, block_size, 8]  (8-element chunks, chunk-major)
                   v_pool [NB, Hkv, D, block_size]       (V transposed within the block)
+    FP8 pools (E4M3 codes, one byte each, block_size 16, D % 64 == 0) have one
+    byte order, again one contiguous run of 16 * D bytes per (block, head):
+      k_pool [NB, Hkv, D/64, 4, 16 tokens, 16]  dims (4i + g) * 16 + w at [i, g, t, w]
+      v_pool [NB, Hkv, D/64, 4, 16, 4, 4]       token 4j + u, dim (4i + b) * 16 + r
+                                                 at [i, j, r, b, u]
 """
 from __future__ import annotations
 
@@ -41,7 +46,7 @@ __all__ = [
     "PrefillInputs", "DecodeInputs", "CONFIGS",
     "prefill_inputs", "blockskip_inputs", "decode_inputs", "shared_prefix_decode_inputs",
     "unshared_copy", "paged_prefill_inputs", "PagedPrefillInputs", "to_dtype",
-    "upcast_f64", "prefill_flops",
+    "upcast_f64", "prefill_flops", "Fp8DecodeInputs", "fp8_decode_inputs",
 ]
 
 
@@ -414,6 +419,66 @@ def unshared_copy(d: DecodeInputs) -> DecodeInputs:
     return dataclasses.replace(d, k_pool=d.k_pool[src].clone(), v_pool=d.v_pool[src].clone(),
                                block_table=torch.from_numpy(new_table),
                                perm=np.arange(len(used)))
+
+
+@dataclasses.dataclass
+class Fp8DecodeInputs:
+    """An FP8 copy of a bf16 decode problem: the K and V pools quantized to
+    E4M3 codes with one scale per pool (code = round(x / scale), saturated to
+    +-448; NaN tail slots stay NaN codes)."""
+    base: DecodeInputs          # the bf16 problem (row-major pools); q, table, lengths
+    k_pool: torch.Tensor        # uint8 [NB, Hkv, 16 * D], FP8 byte order
+    v_pool: torch.Tensor
+    k_scale: float
+    v_scale: float
+    k_codes: torch.Tensor       # uint8 [NB, Hkv, 16, D], the same codes as token rows
+    v_codes: torch.Tensor
+    k_rows: torch.Tensor        # float64 [NB, Hkv, 16, D] = scale * code value (torch's decoding)
+    v_rows: torch.Tensor
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V the decode must read: sum_n L_n * Hkv * D * 2 tensors * 1 byte."""
+        b = self.base
+        return int(b.seq_lens.to(torch.int64).sum()) * b.Hkv * b.D * 2
+
+
+def _fp8_quantize(pool: torch.Tensor):
+    x = pool.to(torch.float32)
+    finite = x[torch.isfinite(x)]
+    amax = float(finite.abs().max()) if finite.numel() else 1.0
+    scale = float(np.float32(max(amax, 1e-30) / 448.0))
+    codes = (x / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    rows = codes.to(torch.float64) * scale
+    return codes.view(torch.uint8), scale, rows
+
+
+def _fp8_byte_order(codes: torch.Tensor, which: str) -> torch.Tensor:
+    NB, Hkv, bs, D = codes.shape
+    if which == "k":   # [NB, Hkv, t, i, g, w] -> [NB, Hkv, i, g, t, w]
+        x = codes.reshape(NB, Hkv, bs, D // 64, 4, 16).permute(0, 1, 3, 4, 2, 5)
+    else:              # [NB, Hkv, j, u, i, b, r] -> [NB, Hkv, i, j, r, b, u]
+        x = codes.reshape(NB, Hkv, 4, 4, D // 64, 4, 16).permute(0, 1, 4, 2, 6, 5, 3)
+    return x.contiguous().reshape(NB, Hkv, bs * D)
+
+
+def fp8_decode_inputs(N: int, Hq: int, Hkv: int, D: int, *, seed: int,
+                      **kw) -> Fp8DecodeInputs:
+    """The decode problem of :func:`decode_inputs` (same draws; bf16 q,
+    row-major pools) with its K and V pools quantized to FP8 E4M3.  Each
+    pool gets scale = max|x| / 448 over its finite entries (as float32), and
+    codes round(x / scale) (round to nearest even, torch's float8_e4m3fn
+    conversion) in the FP8 byte order of the module docstring."""
+    if D % 64:
+        raise ValueError("FP8 pools need D % 64 == 0")
+    kw.pop("layout", None)
+    kw.pop("dtype", None)
+    d = decode_inputs(N, Hq, Hkv, D, seed=seed, layout="rowmajor", dtype="bf16", **kw)
+    if d.block_size != 16:
+        raise ValueError("FP8 pools need block_size 16")
+    kc, ks, kr = _fp8_quantize(d.k_pool)
+    vc, vs, vr = _fp8_quantize(d.v_pool)
+    return Fp8DecodeInputs(base=d, k_pool=_fp8_byte_order(kc, "k"), v_pool=_fp8_byte_order(vc, "v"),
+                           k_scale=ks, v_scale=vs, k_codes=kc, v_codes=vc, k_rows=kr, v_rows=vr)
 
 
 def _to_layout(kp: np.ndarray, vp: np.ndarray, layout: str, bs: int, D: int):
