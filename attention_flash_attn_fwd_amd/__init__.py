@@ -23,8 +23,9 @@ __all__ = [
     "AttnError", "lib_path", "load", "attn_status_string", "attn_arch_supported",
     "attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
     "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_paged_blockskip",
-    "attn_prefill_paged",
+    "attn_prefill_paged", "attn_decode_paged_fp8",
     "prefill", "prefill_blockskip", "decode_paged", "decode_paged_blockskip", "prefill_paged",
+    "decode_paged_fp8",
 ]
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -76,6 +77,9 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_paged_blockskip.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I,
                                                 _I, _I, _I, _F, _F, _P, _P, _P, ctypes.c_size_t,
                                                 _P]
+    lib.attn_decode_paged_fp8.restype = _I
+    lib.attn_decode_paged_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                          _F, _F, _F, _P, ctypes.c_size_t, _P]
     _LIB = lib
     return lib
 
@@ -248,6 +252,34 @@ def attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_
     _check(st, "attn_decode_paged_blockskip")
 
 
+def attn_decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o, lse,
+                          scale: float, k_scale: float, v_scale: float, workspace,
+                          stream=None) -> None:
+    """Paged decode over FP8 (E4M3) pools: uint8 k_pool / v_pool
+    [NB, Hkv, 16 * D] in the byte order of include/attn.h, one scale each."""
+    N, Hq, D = q.shape
+    NB, Hkv = k_pool.shape[0], k_pool.shape[1]
+    _dev(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace)
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise TypeError("FP8 pools are uint8 code tensors")
+    if tuple(k_pool.shape) != (NB, Hkv, block_size * D) or v_pool.shape != k_pool.shape:
+        raise ValueError("FP8 pools must be [NB, Hkv, block_size * D]")
+    if o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != N or seq_lens.shape != (N,):
+        raise ValueError("block_table must be [N, max_blocks], seq_lens [N]")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq)):
+        raise ValueError("lse must be float32 [N,Hq]")
+    st = load().attn_decode_paged_fp8(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), int(block_size),
+        _ptr(o), _ptr(lse), N, Hq, Hkv, D, NB, int(block_table.shape[1]), float(scale),
+        float(k_scale), float(v_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "attn_decode_paged_fp8")
+
+
 def attn_prefill_paged(q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse,
                        max_seqlen_q: int, scale: float, block_size: int = 16, stream=None,
                        layout: str = "rowmajor") -> None:
@@ -343,6 +375,23 @@ def decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, lam: float,
     attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse,
                                 scale, lam, workspace, bm, cnt, layout="mfma")
     return o, lse, bm, cnt
+
+
+def decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, k_scale: float, v_scale: float,
+                     block_size: int = 16, scale: Optional[float] = None, workspace=None):
+    """Allocate O, LSE (and the workspace unless given) and run the paged
+    decode over FP8 pools."""
+    N, Hq, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = attn_decode_workspace_bytes(N, Hq, D, int(block_table.shape[1]), block_size)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    attn_decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse, scale,
+                          k_scale, v_scale, workspace)
+    return o, lse
 
 
 def prefill_paged(q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, max_seqlen_q: int,

@@ -123,7 +123,8 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool,
                   int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
                   int num_blocks, int max_blocks_per_seq, float scale, void* workspace,
                   size_t workspace_bytes, int skip, float lambda, uint8_t* skip_bitmap,
-                  unsigned long long* skipped_blocks, hipStream_t stream) {
+                  unsigned long long* skipped_blocks, int fp8, float k_scale, float v_scale,
+                  hipStream_t stream) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
     return ATTN_ERR_INVALID_ARG;
@@ -132,6 +133,7 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool,
   if (kv_layout != ATTN_KV_ROWMAJOR && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_INVALID_ARG;
   if (skip && !(lambda > 0.f && lambda < 1.f)) return ATTN_ERR_INVALID_ARG;
   if (skip && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_UNSUPPORTED;
+  if (fp8 && (!finite_pos(k_scale) || !finite_pos(v_scale))) return ATTN_ERR_INVALID_ARG;
   if (block_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
@@ -165,6 +167,9 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool,
   a.lambda = lambda;
   a.skip_bitmap = skip_bitmap;
   a.skip_count = skipped_blocks;
+  a.fp8 = fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.n_split = ns;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = a.ws_o + (size_t)num_seqs * Hq * ns * D;
@@ -182,7 +187,7 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       size_t workspace_bytes, hipStream_t stream) {
   return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, kv_layout, o, lse,
                        num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, workspace,
-                       workspace_bytes, 0, 0.f, nullptr, nullptr, stream);
+                       workspace_bytes, 0, 0.f, nullptr, nullptr, 0, 1.f, 1.f, stream);
 }
 
 int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v_pool,
@@ -194,7 +199,19 @@ int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v
                                 size_t workspace_bytes, hipStream_t stream) {
   return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, kv_layout, o, lse,
                        num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, workspace,
-                       workspace_bytes, 1, lambda, skip_bitmap, skipped_blocks, stream);
+                       workspace_bytes, 1, lambda, skip_bitmap, skipped_blocks, 0, 1.f, 1.f,
+                       stream);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                          void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
+                          int num_blocks, int max_blocks_per_seq, float scale, float k_scale,
+                          float v_scale, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, ATTN_KV_MFMA, o,
+                       lse, num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, workspace,
+                       workspace_bytes, 0, 0.f, nullptr, nullptr, 1, k_scale, v_scale, stream);
 }
 
 int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_seqlen_q,

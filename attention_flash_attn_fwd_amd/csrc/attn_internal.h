@@ -61,6 +61,9 @@ struct DecodeArgs {
   float lambda;
   uint8_t* skip_bitmap;            // may be null
   unsigned long long* skip_count;  // may be null
+  // FP8 (E4M3) pools in their own byte order (layout ignored), one scale each
+  int fp8;
+  float k_scale, v_scale;
   float* ws_o;    // [N, Hq, n_split, D]
   float* ws_lse;  // [N, Hq, n_split]
   int n_split;

@@ -63,6 +63,7 @@ struct DecParams {
   float* ws_lse;
   int Hq, Hkv, G, num_blocks, max_blocks, n_split;
   float sl2;
+  float v_scale;  // FP8 pools: V code -> value factor (1 otherwise)
   // block skip only
   float thr;                       // log2(lambda)
   uint8_t* skip_map;               // [N, Hkv, max_blocks] or null
@@ -480,6 +481,181 @@ __global__ __launch_bounds__(64, kDecodeWavesPerSimd) void decode_native_kernel(
   }
 }
 
+// Decode over an FP8 (E4M3) pool with one scale per pool (a quantised KV
+// cache: "TensorRT-LLM：大模型推理加速的工业级引擎", 六大核心优化技术 / 量化
+// lists FP8, and its 深入版解读 names the E4M3/E5M2 encodings; decode time is
+// the KV-cache read from HBM, which FP8 halves).  The pool keeps each
+// (block, head) run in an MFMA-native byte order (16 * D bytes):
+//  * K: 16-byte chunks of 16 dims; chunk c of token t at
+//    (c / 4) * 1024 + ((c % 4) * 16 + t) * 16.  Lane (t = lane % 16, g =
+//    lane / 16) loads 16 bytes at i * 1024 + lane * 16 (1 KiB contiguous per
+//    load): dims (4i + g) * 16 .. +15 of token t, which become the A
+//    fragments of two 8-dim k-steps; Q^T is loaded with the same dims.
+//  * V: for 16-dim block b and token t, the byte of dim b * 16 + r sits at
+//    (b / 4) * 1024 + ((t / 4) * 16 + r) * 16 + (b % 4) * 4 + t % 4, so the
+//    16 bytes of lane (r, g) hold, per block b, the four tokens 4g .. 4g+3
+//    that the 16x16x16 MFMA takes from it (again 1 KiB per load).
+// Codes are widened to bf16 exactly (every E4M3 value is a bf16 value) by
+// the pair conversion; the K scale is folded into the softmax scale and the
+// V scale into the final 1 / l, both in fp32.  Loads run NBUF blocks ahead.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
+  // codes of bytes 0-1 (HI = false) or 2-3 as two bf16; the pair is used as
+  // one 32-bit word (its halves are never extracted one by one)
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(64, kDecodeWavesPerSimd) void decode_fp8_kernel(DecParams p) {
+  constexpr int NKS = D / 32;   // 32-dim k-steps of Q.K^T
+  constexpr int NDB = D / 16;   // 16-dim output blocks of P.V
+  constexpr int NI = D / 64;    // 1 KiB loads per block, K and V each
+  constexpr int RUN = kBlk * D; // bytes of one (block, head) run
+
+  const int kvh = blockIdx.x, split = blockIdx.y, n = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int h = lane & 15, g4 = lane >> 4;
+  const int L = p.seq_lens[n];
+  const int tok_begin = split * kDecodeSplitTokens;
+  if (L <= 0 || tok_begin >= L) return;  // the merge kernel handles L <= 0
+  const int n_tok = min(L - tok_begin, kDecodeSplitTokens);
+  const int G = p.G;
+
+  const int32_t* trow = p.table + (size_t)n * p.max_blocks;
+  const int lb0 = tok_begin / kBlk;
+  const int n_blk = (n_tok + kBlk - 1) / kBlk;
+  const bool in_table = lb0 + n_blk <= p.max_blocks;
+  int my_ph = 0;
+  if (in_table && lane < n_blk) my_ph = trow[lb0 + lane];
+  // Q^T fragment of k-step 2i + j: dims (g4 + 4i) * 16 + j * 8 .. +7
+  bf16x8 qB[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (h < G)
+      qB[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)n * p.Hq + kvh * G + h) * D +
+                                                (g4 + 4 * (ks >> 1)) * 16 + (ks & 1) * 8);
+    else
+      qB[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  const bool lane_ok = lane >= n_blk || (my_ph >= 0 && my_ph < p.num_blocks);
+  const bool bad = !in_table || !__all(lane_ok);
+  const size_t slot = ((size_t)n * p.Hq + kvh * G + h) * p.n_split + split;
+  if (bad) {
+    if (h < G) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = f32x4{NAN, NAN, NAN, NAN};
+      if (g4 == 0) p.ws_lse[slot] = NAN;
+    }
+    return;
+  }
+
+  const size_t blk_stride = (size_t)p.Hkv * RUN;
+  const unsigned char* kbase =
+      reinterpret_cast<const unsigned char*>(p.k_pool) + (size_t)kvh * RUN + lane * 16;
+  const unsigned char* vbase =
+      reinterpret_cast<const unsigned char*>(p.v_pool) + (size_t)kvh * RUN + lane * 16;
+
+  struct Buf {
+    u32x4 k[NI];
+    u32x4 v[NI];
+  };
+  auto load = [&](int j, Buf& b) {
+    const size_t ph = (size_t)__builtin_amdgcn_readlane(my_ph, j);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      b.k[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kbase + ph * blk_stride + i * 1024));
+      b.v[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(vbase + ph * blk_stride + i * 1024));
+    }
+  };
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_used = kUnset, l = 0.f;
+  const float sl2 = p.sl2;
+
+  auto compute = [&](int j, const Buf& b) {
+    // scores S^T (16 tokens x 16 heads): lane (h, g4) gets tokens 4*g4 + i
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t w0 = b.k[i][2 * jj], w1 = b.k[i][2 * jj + 1];
+        const u32x4 kw = {fp8_pair<false>(w0), fp8_pair<true>(w0), fp8_pair<false>(w1),
+                          fp8_pair<true>(w1)};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw),
+                                                    qB[2 * i + jj], s, 0, 0, 0);
+      }
+    // slots past the sequence end: no score, and a zero code (+0) for their
+    // V (the bytes there may be anything, NaN codes included).  Branch-free,
+    // so no read of the MFMA result follows a branch.
+    const int valid = n_tok - j * kBlk;
+    uint32_t vkeep = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = 4 * g4 + i < valid;
+      s[i] = ok ? s[i] : -INFINITY;
+      vkeep |= ok ? (0xffu << (8 * i)) : 0u;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    const float tmx = half_swap_max(mx) * sl2;
+    if (__any(tmx > m_used + 8.f)) {  // lazy rescale (exponent reference moves by > 2^8)
+      const float m_new = fmaxf(m_used, tmx);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float nm = -m_used;
+    const uint32_t pk0 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[0], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[1], sl2, nm)));
+    const uint32_t pk1 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[2], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[3], sl2, nm)));
+    l += __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk0), kOnes2, 0.f, false) +
+         __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk1), kOnes2, 0.f, false);
+    const u32x2 pw = {pk0, pk1};
+    const s16x4 pB = __builtin_bit_cast(s16x4, pw);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint32_t w = b.v[db >> 2][db & 3] & vkeep;
+      const u32x2 vw = {fp8_pair<false>(w), fp8_pair<true>(w)};
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vw), pB,
+                                                          acc[db], 0, 0, 0);
+    }
+  };
+
+  // NBUF buffers with fixed registers, loads NBUF blocks ahead
+  Buf buf[NBUF];
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u)
+    if (u < n_blk) load(u, buf[u]);
+  for (int j = 0; j < n_blk; j += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (j + u < n_blk) {
+        compute(j + u, buf[u]);
+        if (j + u + NBUF < n_blk) load(j + u + NBUF, buf[u]);
+      }
+    }
+  }
+
+  float lt = l + __shfl_xor(l, 16);
+  lt = half_swap_add(lt);
+  if (h < G) {
+    const float inv = p.v_scale / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = acc[db] * inv;
+    if (g4 == 0) p.ws_lse[slot] = m_used + __log2f(lt);
+  }
+}
+
 // Decode with block skipping ("高效部署稀疏注意力加速方案：BLASST方法详解与实践
 // 指南", 架构与组件: blocks whose scores are negligible next to the running
 // maximum of the blockwise online softmax lose their exp, their V load and
@@ -751,8 +927,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const DecParams& p, int N, int layout, bool skip, hipStream_t stream) {
-  if (skip)
+hipError_t launch_d(const DecParams& p, int N, int layout, bool skip, bool fp8,
+                    hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL((decode_fp8_kernel<D, 4>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
+  else if (skip)
     hipLaunchKernelGGL((decode_skip_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
   else if (layout == 1)
     hipLaunchKernelGGL((decode_native_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
@@ -782,16 +961,19 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.num_blocks = a.num_blocks;
   p.max_blocks = a.max_blocks;
   p.n_split = a.n_split;
-  p.sl2 = a.scale * 1.4426950408889634f;
+  // FP8 pools: the K scale multiplies every score, the V scale the output
+  p.sl2 = a.scale * (a.fp8 ? a.k_scale : 1.f) * 1.4426950408889634f;
+  p.v_scale = a.fp8 ? a.v_scale : 1.f;
   p.G = a.Hq / a.Hkv;
   p.thr = a.skip ? (float)(log((double)a.lambda) * 1.4426950408889634) : 0.f;
   p.skip_map = a.skip_bitmap;
   p.skip_count = a.skip_count;
   if (p.G > 16) return hipErrorInvalidValue;
   if (a.skip && a.layout != 1) return hipErrorInvalidValue;
-  const bool sk = a.skip != 0;
-  return a.D == 64 ? launch_d<64>(p, a.N, a.layout, sk, stream)
-                   : launch_d<128>(p, a.N, a.layout, sk, stream);
+  if (a.fp8 && a.skip) return hipErrorInvalidValue;
+  const bool sk = a.skip != 0, f8 = a.fp8 != 0;
+  return a.D == 64 ? launch_d<64>(p, a.N, a.layout, sk, f8, stream)
+                   : launch_d<128>(p, a.N, a.layout, sk, f8, stream);
 }
 
 }  // namespace attn

@@ -81,7 +81,8 @@ def main():
 
     import attention_flash_attn_fwd_amd as A
     from workloads import (CONFIGS, blockskip_inputs, decode_inputs, paged_prefill_inputs,
-                           prefill_flops, prefill_inputs, shared_prefix_decode_inputs)
+                           prefill_flops, prefill_inputs, shared_prefix_decode_inputs,
+                           fp8_decode_inputs)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -189,6 +190,28 @@ def main():
             "frac_hbm_peak": round(kv_bytes / mr / 1e9 / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(mr * 1e6, 2)}
         del rpools
+
+        # the same cache with FP8 (E4M3) pools, one fp32 scale per pool: half
+        # the bytes per cached element (q, table and lengths are the same)
+        f8 = fp8_decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"],
+                               lmin=cd["lmin"], lmax=cd["lmax"])
+        fpools = [(f8.k_pool.to(dev), f8.v_pool.to(dev)) for _ in range(2)]
+        fctr = [0]
+
+        def run_fp8():
+            kp, vp = fpools[fctr[0] % 2]
+            fctr[0] += 1
+            A.attn_decode_paged_fp8(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, f8.k_scale,
+                                    f8.v_scale, ws)
+        mf = time_it(run_fp8, 20)
+        fbytes = f8.kv_bytes()
+        secondary["paged_decode_gqa_fp8_kv"] = {
+            "kv_GBps": round(fbytes / mf / 1e9, 1),
+            "frac_hbm_peak": round(fbytes / mf / 1e9 / PEAK_HBM_GBPS, 4),
+            "us_per_launch": round(mf * 1e6, 2), "kv_bytes": fbytes,
+            "speedup_vs_bf16_kv": round(dec_s / mf, 3),
+            "note": "E4M3 codes, one fp32 scale per pool; same q, table and lengths"}
+        del fpools
 
         # shared prompts (copy-on-write block tables): 16 prompts of 1536
         # tokens, 4 samples each with U[1, 2048] own tokens; the kernel reads

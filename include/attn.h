@@ -212,6 +212,33 @@ int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v
                                 unsigned long long* skipped_blocks, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* Paged decode over an FP8 KV cache.  The TensorRT-LLM page lists FP8 among
+ * its low-precision formats ("TensorRT-LLM：大模型推理加速的工业级引擎",
+ * 六大核心优化技术 / 量化; its 深入版解读 names the E4M3/E5M2 encodings) and the
+ * integration page enables FP8 with the KV cache ("flash-attention与TensorRT-
+ * LLM集成", 案例研究：Mistral-7B部署); neither gives a scale convention, so this entry
+ * point takes E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * no infinities, S.1111.111 is NaN, largest finite 448) with ONE fp32 scale per
+ * pool: cached K value = k_scale * code value, V value = v_scale * code value.
+ * The attention is then exactly that of attn_decode_paged on those values.
+ * Arguments as attn_decode_paged (no kv_layout), except:
+ *   k_pool, v_pool : uint8 codes, [num_blocks, Hkv, 16 * D], one run of 16 * D
+ *                    bytes per (block, K/V head), D % 64 == 0, in this order
+ *                    (token t in [0, 16), dim d, c = d / 16):
+ *                      K code at (c / 4) * 1024 + ((c % 4) * 16 + t) * 16 + d % 16
+ *                      V code at (c / 4) * 1024 + ((t / 4) * 16 + d % 16) * 16
+ *                                + (c % 4) * 4 + t % 4
+ *   k_scale, v_scale: finite and > 0 (ATTN_ERR_INVALID_ARG otherwise)
+ * q, o stay bf16 and lse fp32.  Slots past a sequence's end may hold any
+ * byte, NaN codes included; they are never used.  Same device-side rules,
+ * workspace and errors as attn_decode_paged. */
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                          void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
+                          int num_blocks, int max_blocks_per_seq, float scale, float k_scale,
+                          float v_scale, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Chunked / variable-length causal prefill over the paged KV cache (the
  * prefill-with-KV-cache case of "flash-attention与TensorRT-LLM集成" and the
  * block table of "LLM推理优化技术综述", PageAttention part).  Sequence n

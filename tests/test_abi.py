@@ -26,6 +26,7 @@ def test_header_lists_the_entry_points():
     names = _declared()
     for need in ("attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
                  "attn_decode_paged", "attn_decode_paged_blockskip", "attn_prefill_paged",
+                 "attn_decode_paged_fp8",
                  "attn_decode_workspace_bytes", "attn_status_string", "attn_arch_supported"):
         assert need in names
 
@@ -158,3 +159,28 @@ def test_prefill_paged_validation_without_device():
     assert call(lay=1) == -2           # MFMA-native pools: not supported here
     assert call(bs=32) == -2
     assert call(D=96) == -2
+
+
+def test_decode_fp8_validation_without_device():
+    lib = A.load()
+    need = A.attn_decode_workspace_bytes(2, 8, 128, 4, 16)
+
+    def call(**kw):
+        a = dict(q=8, kp=8, vp=8, bt=8, sl=8, bs=16, o=8, N=2, Hq=8, Hkv=2, D=128, NB=8, MB=4,
+                 scale=0.1, ks=0.01, vs=0.02, ws=256, wsb=need)
+        a.update(kw)
+        return lib.attn_decode_paged_fp8(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["bs"],
+                                         a["o"], None, a["N"], a["Hq"], a["Hkv"], a["D"], a["NB"],
+                                         a["MB"], a["scale"], a["ks"], a["vs"], a["ws"], a["wsb"],
+                                         None)
+    assert call(ks=0.0) == -1
+    assert call(vs=-1.0) == -1
+    assert call(ks=float("nan")) == -1
+    assert call(vs=float("inf")) == -1
+    assert call(kp=None) == -1
+    assert call(Hq=6, Hkv=4) == -1
+    assert call(bs=32) == -2
+    assert call(D=96) == -2
+    assert call(Hq=64, Hkv=2) == -2
+    assert call(ws=None) == -4
+    assert call(wsb=need - 1) == -4

@@ -384,3 +384,78 @@ def test_blockskip_full_config_sampled_qtiles():
     nT = c["S"] // 64
     live = c["B"] * c["Hq"] * nT * (nT + 1) // 2
     say(f"c5 skipped fraction {cnt / live:.6f} ({cnt}/{live})")
+
+
+# ------------------------------------------------------------ FP8 KV decode
+
+def _run_decode_fp8(f, table=None, lens=None, k_pool=None, v_pool=None):
+    dev = "cuda"
+    b = f.base
+    bt = (b.block_table if table is None else table).to(dev)
+    sl = (b.seq_lens if lens is None else lens).to(dev)
+    kp = (f.k_pool if k_pool is None else k_pool).to(dev)
+    vp = (f.v_pool if v_pool is None else v_pool).to(dev)
+    o, lse = A.decode_paged_fp8(b.q.to(dev), kp, vp, bt, sl, f.k_scale, f.v_scale,
+                                scale=b.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _ref_decode_fp8(f, table=None, lens=None):
+    from oracle import ref_decode_paged_fp8
+    b = f.base
+    bt = (b.block_table if table is None else table).numpy()
+    sl = (b.seq_lens if lens is None else lens).numpy()
+    return ref_decode_paged_fp8(upcast_f64(b.q), f.k_pool.numpy(), f.v_pool.numpy(), bt, sl, 16,
+                                b.scale, f.k_scale, f.v_scale)
+
+
+def test_paged_decode_fp8_full_config_nan_tails():
+    from workloads import fp8_decode_inputs
+    c = CONFIGS["paged_decode_gqa"]
+    say("paged_decode_gqa full config with FP8 (E4M3) pools, NaN codes in tail slots")
+    f = fp8_decode_inputs(c["N"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], lmin=c["lmin"],
+                          lmax=c["lmax"], tail="nan")
+    o, lse = _run_decode_fp8(f)
+    ro, rl = _ref_decode_fp8(f)
+    _compare(o, lse, ro, rl, TOL["bf16"], "decode fp8 c4")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 128), (16, 1, 64), (8, 4, 64),
+                                       (32, 2, 128)])
+def test_paged_decode_fp8_edge_lengths(Hq, Hkv, D):
+    from workloads import fp8_decode_inputs
+    lens = [1, 15, 16, 17, 63, 64, 65, 511, 512, 513, 1000, 0, 1024, 1025, 1537]
+    say(f"decode fp8 edge lengths Hq{Hq} Hkv{Hkv} D{D} lens={lens}")
+    f = fp8_decode_inputs(len(lens), Hq, Hkv, D, seed=190 + D, lens=lens, tail="nan")
+    o, lse = _run_decode_fp8(f)
+    ro, rl = _ref_decode_fp8(f)
+    z = lens.index(0)
+    assert np.all(o[z] == 0) and np.all(np.isneginf(lse[z]))
+    keep = [i for i in range(len(lens)) if lens[i] > 0]
+    _compare(o[keep], lse[keep], ro[keep], rl[keep], TOL["bf16"], "decode fp8 edges")
+
+
+def test_paged_decode_fp8_permutation_bit_identical_and_bad_entries():
+    from workloads import fp8_decode_inputs
+    say("decode fp8: physical block permutation is bit-identical; bad table entries give NaN")
+    f = fp8_decode_inputs(8, 32, 8, 128, seed=177, lmin=1, lmax=700)
+    o1, l1 = _run_decode_fp8(f)
+    b = f.base
+    perm = torch.from_numpy(np.random.default_rng(178).permutation(b.num_blocks))
+    kp2 = torch.empty_like(f.k_pool); kp2[perm] = f.k_pool
+    vp2 = torch.empty_like(f.v_pool); vp2[perm] = f.v_pool
+    bt = b.block_table.clone()
+    m = bt >= 0
+    bt[m] = perm[bt[m].long()].to(torch.int32)
+    o2, l2 = _run_decode_fp8(f, table=bt, k_pool=kp2, v_pool=vp2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ro, rl = _ref_decode_fp8(f)
+    _compare(o1, l1, ro, rl, TOL["bf16"], "decode fp8 perm")
+    bt = b.block_table.clone()
+    used = int((bt[1] >= 0).sum())
+    bt[1, used - 1] = b.num_blocks + 3
+    o3, l3 = _run_decode_fp8(f, table=bt)
+    assert np.isnan(o3[1]).all() and np.isnan(l3[1]).all()
+    rows = [0] + list(range(2, 8))
+    _compare(o3[rows], l3[rows], ro[rows], rl[rows], TOL["bf16"], "decode fp8 good rows")
