@@ -46,10 +46,15 @@ def short_name(name: str) -> str:
     return s[:i] if i > 0 else s
 
 
-def kernel_rows(db_path: str):
+def kernel_rows(db_path: str, by_grid: bool = False):
     cur = sqlite3.connect(db_path).cursor()
-    q = """select name, count(*), avg(duration), min(duration), max(duration), sum(duration)
-           from kernels group by name order by sum(duration) desc"""
+    if by_grid:
+        q = """select name || ' [' || grid_x || 'x' || grid_y || 'x' || grid_z || ']', count(*),
+                      avg(duration), min(duration), max(duration), sum(duration)
+               from kernels group by name, grid_x, grid_y, grid_z order by sum(duration) desc"""
+    else:
+        q = """select name, count(*), avg(duration), min(duration), max(duration), sum(duration)
+               from kernels group by name order by sum(duration) desc"""
     return list(cur.execute(q))
 
 
@@ -91,12 +96,15 @@ def cmd_copy(a):
 
 
 def cmd_trace(a):
-    rows = kernel_rows(find_db(a.db))
+    rows = kernel_rows(find_db(a.db), a.by_grid)
     tot = sum(r[5] for r in rows) or 1
+    w = 64 if a.by_grid else 48
     out = [a.title, "", "Command (repo root, TMPDIR=/tmp):", "  " + a.cmd, "",
-           f"{'kernel':<48} {'calls':>5} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+           f"{'kernel' + (' [grid]' if a.by_grid else ''):<{w}} {'calls':>5} {'avg_us':>9} "
+           f"{'min_us':>9} {'max_us':>9} {'pct':>6}"]
     for n, c, av, mn, mx, s in rows:
-        out.append(f"{short_name(n)[:48]:<48} {c:>5} {av / 1e3:>9.2f} {mn / 1e3:>9.2f} "
+        name = short_name(n.split(' [')[0]) + (' [' + n.split(' [')[1] if ' [' in n else '')
+        out.append(f"{name[:w]:<{w}} {c:>5} {av / 1e3:>9.2f} {mn / 1e3:>9.2f} "
                    f"{mx / 1e3:>9.2f} {100 * s / tot:>6.2f}")
     if a.note:
         out += ["", a.note]
@@ -161,6 +169,8 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--title", required=True)
     t.add_argument("--note", default="")
+    t.add_argument("--by-grid", action="store_true",
+                   help="one row per (kernel, grid) instead of per kernel")
     t.add_argument("--out", required=True)
     r = sp.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
