@@ -4,13 +4,14 @@
 
 One step = one pass over the hot path's two entry points: the causal MHA
 prefill at the Llama-2-7B attention shape (B=4, Hq=Hkv=32, S=2048, D=128,
-bf16) followed by the paged GQA decode (64 sequences, lengths U[512,4096],
-Hq=32, Hkv=8, D=128, 16-token blocks).  Inputs are seeded synthetic tensors
-already resident in HBM.  W untimed warm-up steps, then exactly K timed steps
-bracketed by device synchronisations: the K prefills back to back, then the
-K decodes, with HIP events before, between and after them on the stream the
-kernels run on, which gives each kernel's mean launch duration without
-per-launch marker gaps.  Prints ONE JSON line.
+bf16) and the paged GQA decode (64 sequences, lengths U[512,4096], Hq=32,
+Hkv=8, D=128, 16-token blocks, row-major [block, head, slot, dim] pools; the
+MFMA-native pools are timed under "secondary").  Inputs are seeded synthetic
+tensors already resident in HBM.  W untimed warm-up steps, then exactly K
+timed steps bracketed by device synchronisations: the K decodes back to
+back, then the K prefills, with HIP events before, between and after them on
+the stream the kernels run on, which gives each kernel's mean launch
+duration without per-launch marker gaps.  Prints ONE JSON line.
 
 `value` is the prefill throughput in TFLOP/s (algorithmic flops
 4*B*Hq*D*S(S+1)/2 over the prefill kernel's mean event time).  The decode
@@ -100,7 +101,7 @@ def main():
 
     cd = CONFIGS["paged_decode_gqa"]
     wd = decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"], lmin=cd["lmin"],
-                       lmax=cd["lmax"], block_size=cd["block_size"], layout="mfma")
+                       lmax=cd["lmax"], block_size=cd["block_size"])
     dq = wd.q.to(dev)
     # two copies of the pool (2 x 623 MB), used alternately, for the same reason
     pools = [(wd.k_pool.to(dev), wd.v_pool.to(dev)) for _ in range(2)]
@@ -117,14 +118,17 @@ def main():
 
     def run_decode(i):
         kp, vp = pools[i % 2]
-        A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws, layout="mfma")
+        A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws)
 
     # ------------------------------------------------------------ timed steps
-    # K steps = K prefills and K decodes.  The prefills are issued back to
-    # back, then the decodes, with one HIP event before, between and after,
+    # K steps = K decodes and K prefills.  The decodes are issued back to
+    # back, then the prefills, with one HIP event before, between and after,
     # all on the stream the kernels are launched on (torch's current stream,
     # passed through the C ABI).  A marker between every pair of launches
-    # would add an idle gap of about 10 us in front of each kernel.
+    # would add an idle gap of about 10 us in front of each kernel.  The
+    # decodes go first: right after a burst of back-to-back prefills the
+    # chip's power state slows the memory-bound decode by about 5%, which a
+    # measurement of the decode kernel should not include.
     for i in range(args.warmup):
         run_prefill(i)
         run_decode(i)
@@ -138,15 +142,15 @@ def main():
     torch.cuda._sleep(GPU_SPIN_CYCLES)
     e0.record()
     for i in range(args.steps):
-        run_prefill(i)
+        run_decode(i)
     e1.record()
     for i in range(args.steps):
-        run_decode(i)
+        run_prefill(i)
     e2.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_s = e0.elapsed_time(e1) * 1e-3 / args.steps
-    dec_s = e1.elapsed_time(e2) * 1e-3 / args.steps
+    dec_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    pre_s = e1.elapsed_time(e2) * 1e-3 / args.steps
     pre_tflops = p_flops / pre_s / 1e12
     dec_gbps = kv_bytes / dec_s / 1e9
 
@@ -154,8 +158,8 @@ def main():
         "paged_decode_gqa": {
             "kv_GBps": round(dec_gbps, 1), "frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(dec_s * 1e6, 2),
-            "kv_bytes": kv_bytes, "launches": "decode_native + decode_merge", "pool_layout": "mfma",
-            "traffic": measured_traffic("decode_native"),
+            "kv_bytes": kv_bytes, "launches": "decode_split + decode_merge",
+            "pool_layout": "rowmajor", "traffic": measured_traffic("decode_split"),
         },
     }
 
@@ -174,21 +178,23 @@ def main():
         return a.elapsed_time(b) * 1e-3 / reps
 
     if not args.no_secondary:
-        # the same cache in the row-major pool layout (LDS-staged kernel)
+        # the same cache in the MFMA-native pool layout (register-direct kernel)
         wr = decode_inputs(cd["N"], cd["Hq"], cd["Hkv"], cd["D"], seed=cd["seed"],
-                           lmin=cd["lmin"], lmax=cd["lmax"], block_size=cd["block_size"])
+                           lmin=cd["lmin"], lmax=cd["lmax"], block_size=cd["block_size"],
+                           layout="mfma")
         rpools = [(wr.k_pool.to(dev), wr.v_pool.to(dev)) for _ in range(2)]
         ctr = [0]
 
-        def run_rowmajor():
+        def run_native():
             kp, vp = rpools[ctr[0] % 2]
             ctr[0] += 1
-            A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws)
-        mr = time_it(run_rowmajor, 20)
-        secondary["paged_decode_gqa_rowmajor_pools"] = {
+            A.attn_decode_paged(dq, kp, vp, dbt, dsl, 16, do, dlse, wd.scale, ws, layout="mfma")
+        mr = time_it(run_native, 20)
+        secondary["paged_decode_gqa_mfma_pools"] = {
             "kv_GBps": round(kv_bytes / mr / 1e9, 1),
             "frac_hbm_peak": round(kv_bytes / mr / 1e9 / PEAK_HBM_GBPS, 4),
-            "us_per_launch": round(mr * 1e6, 2)}
+            "us_per_launch": round(mr * 1e6, 2), "launches": "decode_native + decode_merge",
+            "traffic": measured_traffic("decode_native")}
         del rpools
 
         # the same cache with FP8 (E4M3) pools, one fp32 scale per pool: half
