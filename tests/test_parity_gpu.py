@@ -80,6 +80,21 @@ def test_prefill_bf16_small(B, Hq, Hkv, S, D, causal):
     _compare(o, lse, ro, rl, TOL["bf16"], "small")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal", [
+    (1, 8, 2, 2065, 128, True),    # most tiles in the steady-state loop, ragged tail
+    (1, 8, 8, 1500, 128, False),   # non-causal MHA, ragged tail
+    (2, 8, 8, 1100, 64, True),     # D=64 over many tiles
+    (1, 32, 4, 1024, 128, True),   # groups of 8 query heads, 32-row workgroup slices
+])
+def test_prefill_bf16_medium_all_rows(B, Hq, Hkv, S, D, causal):
+    say(f"prefill bf16 medium, every row: B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} causal={causal}")
+    w = prefill_inputs(B, Hq, Hkv, S, D, seed=21 + S, causal=causal)
+    o, lse = _run_prefill(w)
+    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=causal,
+                         scale=w.scale)
+    _compare(o, lse, ro, rl, TOL["bf16"], "medium")
+
+
 def test_prefill_f32_variants():
     for (B, Hq, Hkv, S, D, causal) in [(1, 4, 2, 77, 128, True), (2, 2, 1, 50, 64, False)]:
         say(f"prefill f32 B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} causal={causal}")
@@ -109,6 +124,16 @@ def test_prefill_full_size_sampled_rows(name):
     _compare(o[:, :, rows], lse[:, :, rows], ro, rl, TOL["bf16"], name)
     # property at every row: |O| is bounded by max |V| of the visible prefix
     assert np.abs(o).max() <= float(w.v.float().abs().max()) + 1e-2
+
+
+def test_prefill_noncausal_gqa_s8192_sampled_rows():
+    say("non-causal GQA B1 Hq32 Hkv8 S8192 D128, sampled rows")
+    w = prefill_inputs(1, 32, 8, 8192, 128, seed=1013, causal=False)
+    o, lse = _run_prefill(w)
+    rows = _sampled_rows(8192, 32, 9)
+    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=False,
+                         scale=w.scale, rows=rows)
+    _compare(o[:, :, rows], lse[:, :, rows], ro, rl, TOL["bf16"], "noncausal s8192")
 
 
 # -------------------------------------------------------------------- decode
