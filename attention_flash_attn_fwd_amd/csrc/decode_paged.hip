@@ -875,15 +875,28 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 
 // One wave per (query head, sequence).  The lanes own splits while the
 // weights are formed (max and sum are wave reductions), then own D/64
-// output dims each while the weighted partial outputs are summed; the loads
-// of different splits are independent, so they are all in flight together.
+// output dims each while the weighted partial outputs are summed.  The
+// sequence length, the first 64 splits' log-sum-exps and the first CH
+// splits' partial outputs do not depend on each other, so they are loaded
+// together before anything is decided (one memory round trip for up to CH
+// splits); workspace slots past the sequence's splits hold stale values
+// and are only ever selected away, never multiplied.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecParams p) {
   constexpr int DPL = D / 64;  // output dims per lane
+  constexpr int CH = 8;        // splits whose partial outputs are loaded at once
   const int h = blockIdx.x, n = blockIdx.y, lane = threadIdx.x;
-  const int L = p.seq_lens[n];
   const size_t out = (size_t)n * p.Hq + h;
   uint16_t* orow = p.o + out * D + lane * DPL;
+  const float* lse_s = p.ws_lse + out * p.n_split;
+  const float* o_s = p.ws_o + out * p.n_split * D + lane * DPL;
+  const int L = p.seq_lens[n];
+  const float lse0 = lane < p.n_split ? lse_s[lane] : kUnset;
+  float part[CH][DPL];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) part[c][e] = c < p.n_split ? o_s[(size_t)c * D + e] : 0.f;
   if (L <= 0 || (long long)L > (long long)p.max_blocks * kBlk) {
     const uint16_t fill = L == 0 ? 0 : to_bf16(NAN);
 #pragma unroll
@@ -892,26 +905,50 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecParams p) {
     return;
   }
   const int ns = (L + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
-  const float* lse_s = p.ws_lse + out * p.n_split;
-  const float* o_s = p.ws_o + out * p.n_split * D + lane * DPL;
-  float M = kUnset;
-  bool bad = false;
-  for (int s = lane; s < ns; s += 64) {
+  float M = lane < ns ? lse0 : kUnset;
+  bool bad = lane < ns && lse0 != lse0;
+  for (int s = lane + 64; s < ns; s += 64) {
     const float v = lse_s[s];
     bad |= (v != v);
     M = fmaxf(M, v);
   }
   M = wave_max(M);
   bad = __any(bad);
-  float W = 0.f;
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
+  // first 64 splits: weights from the loaded log-sum-exps
+  const float w0 = lane < ns ? __builtin_amdgcn_exp2f(lse0 - M) : 0.f;
+  float W = w0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (c < ns) {
+      const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w0), c));
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wi, part[c][e], acc[e]);
+    }
+  }
+  for (int c0 = CH; c0 < min(ns, 64); c0 += CH) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e)
+        part[c][e] = c0 + c < ns ? o_s[(size_t)(c0 + c) * D + e] : 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c0 + c < ns) {
+        const float wi =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w0), c0 + c));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wi, part[c][e], acc[e]);
+      }
+    }
+  }
+  // splits past the first 64 (sequences longer than 64 * 512 tokens)
+  for (int s0 = 64; s0 < ns; s0 += 64) {
     const float w = s0 + lane < ns ? __builtin_amdgcn_exp2f(lse_s[s0 + lane] - M) : 0.f;
     W += w;
     const int cnt = min(64, ns - s0);
-#pragma unroll 8
     for (int i = 0; i < cnt; ++i) {
       const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i));
       const float* src = o_s + (size_t)(s0 + i) * D;

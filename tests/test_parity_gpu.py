@@ -484,3 +484,20 @@ def test_paged_decode_fp8_permutation_bit_identical_and_bad_entries():
     assert np.isnan(o3[1]).all() and np.isnan(l3[1]).all()
     rows = [0] + list(range(2, 8))
     _compare(o3[rows], l3[rows], ro[rows], rl[rows], TOL["bf16"], "decode fp8 good rows")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS + ["fp8"])
+def test_paged_decode_long_sequences_many_splits(layout):
+    """Sequences of 9, 18 and 79 splits (the merge's chunked and >64-split paths)."""
+    lens = [4097, 9000, 40000]
+    say(f"decode long sequences {lens} ({layout})")
+    if layout == "fp8":
+        from workloads import fp8_decode_inputs
+        f = fp8_decode_inputs(3, 16, 4, 128, seed=303, lens=lens, tail="nan")
+        o, lse = _run_decode_fp8(f)
+        ro, rl = _ref_decode_fp8(f)
+    else:
+        d = decode_inputs(3, 16, 4, 128, seed=303, lens=lens, tail="nan", layout=layout)
+        o, lse = _run_decode(d)
+        ro, rl = _ref_decode(d)
+    _compare(o, lse, ro, rl, TOL["bf16"], f"decode long ({layout})")
