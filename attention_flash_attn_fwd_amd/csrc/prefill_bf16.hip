@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-  __shared__ int skip_flag[2][kWaves];
+  __shared__ int vote_lds[2][kWaves];  // block skip: (tile << 1) | negligible
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,10 +174,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   const int sub = hg % p.sub_per_kv;
   const int bk = hg / p.sub_per_kv;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
-  // Waves w and w+4 share a SIMD.  Without block skip they run the tile
-  // loop half an iteration apart (see below), so they get adjacent 32-row
-  // slots: equal causal tile counts keep both busy to the end.
-  const int slot = SKIP ? wave : ((wave & 3) << 1) | (wave >> 2);
+  // Waves w and w+4 share a SIMD and run the tile loop half an iteration
+  // apart (see below), so they get adjacent 32-row slots: equal causal tile
+  // counts keep both busy to the end.  With block skip, the two waves of a
+  // 64-row skip tile (slots s and s ^ gw) must run in the same half; this
+  // mapping gives that for gw >= 2, and slot = wave (pairing waves 2k and
+  // 2k+1) for gw == 1.
+  const int slot = (SKIP && p.gw == 1) ? wave : ((wave & 3) << 1) | (wave >> 2);
+  const int pslot = slot ^ p.gw;  // block skip: the other half of this skip tile
+  const int pwave = (SKIP && p.gw == 1) ? pslot : ((pslot & 1) << 2) | (pslot >> 1);
   const int head = kvh * p.G + sub * p.gw + (slot % p.gw);
   const int row0 = qblk * p.rows_per_wg;
   const int q0 = row0 + (slot / p.gw) * 32;
@@ -441,25 +446,31 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   };
-  auto finish = [&](int t, f32x16* sc, float tmx) {
-    uint32_t pk[2][8];
-    softmax(sc, tmx, pk);
-    pv(t, pk);
-  };
-  // block-skip vote of this wave's 32 rows for key tile t, published in LDS
-  auto publish_vote = [&](int t, float tmx_t) {
+  // block skip: this wave's vote on key tile t (are all 32 of its rows
+  // negligible?), published in LDS; the other wave of the 64-row tile runs
+  // the same phase, so its vote on t arrives within a few instructions (the
+  // wait is bounded; past the bound the tile is kept).  One wave of the pair
+  // records the decisions on its live tiles; its bitmap store is a
+  // vector-memory operation that the phase's copy wait has to count.  True
+  // if tile t is skipped.
+  const bool records = SKIP && ((slot / p.gw) & 1) == 0;
+  auto vote_pair = [&](int t, float tmx_t) -> bool {
     bool neg = true;
     if (t < wave_tiles)
       neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < p.thr) ||
             (q0 + n >= S);
     const bool all_neg = __all(neg);
-    if (lane == 0) skip_flag[t & 1][wave] = all_neg ? 1 : 0;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  };
-  // read the pair's votes for tile t; record the decision; true if skipped
-  auto decide = [&](int t) -> bool {
-    const bool sk = skip_flag[t & 1][wave] && skip_flag[t & 1][wave ^ p.gw];
-    if (((wave / p.gw) & 1) == 0) {
+    if (lane == 0)
+      __hip_atomic_store(&vote_lds[t & 1][wave], (t << 1) | (all_neg ? 1 : 0), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+    int other = -1;
+    for (int spin = 0; spin < (1 << 16); ++spin) {
+      other = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+          &vote_lds[t & 1][pwave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+      if ((other >> 1) == t) break;
+    }
+    const bool sk = all_neg && (other >> 1) == t && (other & 1);
+    if (records && t < wave_tiles) {
       if (lane == 0 && p.skip_map)
         p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = sk ? 1 : 0;
       skipped += sk ? 1u : 0u;
@@ -522,27 +533,45 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     for (; j <= n_tiles; ++j) general(j);
     if (grp == 0) block_barrier();
   } else {
-    // Block skip: the decision on a 64-row tile needs the row maxima of both
-    // of its waves, published in LDS, so every wave scores tile t, votes,
-    // and finishes tile t-1 after the next barrier.
-    float tmx_prev = -INFINITY;
-    for (int t = 0; t < n_tiles; ++t) {
-      if (t + 1 < n_tiles) wait_all_but_newest(); else wait_vmem<0>();
-      block_barrier();
-      if (t + 2 < n_tiles) issue(t + 2);
-      if (t >= 1 && t - 1 < wave_tiles) {
-        if (!decide(t - 1)) finish(t - 1, sc, tmx_prev);
-        m_true = fmaxf(m_true, tmx_prev);
-      }
-      if (t < wave_tiles) {
-        qk(t, sc);
-        tmx_prev = row_max(t, sc);
-      }
-      publish_vote(t, tmx_prev);
+    // Block skip, in the same ping-pong.  In its VALU phase j a wave takes
+    // the row maxima of tile j, votes, and waits for the vote of the other
+    // wave of the 64-row tile (same group, same phase).  A skipped tile loses
+    // its softmax now and its P.V in the next MFMA phase; the running max of
+    // the decisions (m_true) takes every tile, skipped or not.
+    const int grp = wave >> 2;
+    uint32_t pk[2][8];
+    bool skip_prev = false;
+    if (lane == 0) {
+      vote_lds[0][wave] = -2;
+      vote_lds[1][wave] = -2;
     }
     block_barrier();
-    const int t = n_tiles - 1;
-    if (t < wave_tiles && !decide(t)) finish(t, sc, tmx_prev);
+    if (grp == 1) {
+      if (2 < n_tiles) issue(2);
+      block_barrier();
+    }
+    for (int j = 0; j <= n_tiles; ++j) {
+      if (j >= 1 && j - 1 < wave_tiles && !skip_prev) pv(j - 1, pk);
+      if (j < wave_tiles) qk(j, sc);
+      block_barrier();
+      const bool issues = j + 2 + grp < n_tiles;
+      if (issues) issue(j + 2 + grp);
+      if (j < n_tiles) {
+        const float tmx = j < wave_tiles ? row_max(j, sc) : -INFINITY;
+        const bool sk = vote_pair(j, tmx);
+        m_true = fmaxf(m_true, tmx);
+        if (j < wave_tiles && !sk) softmax(sc, tmx, pk);
+        skip_prev = sk;
+      }
+      // a bitmap store made in this phase follows the copies just issued
+      const bool stored = records && p.skip_map && j < wave_tiles;
+      if (!issues) wait_vmem<0>();
+      else if (!stored) wait_all_but_newest();
+      else if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 1>();
+      else wait_vmem<DMA_HI + 1>();
+      block_barrier();
+    }
+    if (grp == 0) block_barrier();
   }
 
   if (SKIP && lane == 0 && skipped && p.skip_count)
