@@ -58,8 +58,8 @@ def measured_traffic(kernel: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the GQA-8192 and block-skip measurements")
@@ -129,6 +129,9 @@ def main():
     # decodes go first: right after a burst of back-to-back prefills the
     # chip's power state slows the memory-bound decode by about 5%, which a
     # measurement of the decode kernel should not include.
+    # The chip's clocks rise over roughly the first 10 ms of sustained load
+    # (a prefill measured right after 1.5 ms of warm-up ran about 10% slower
+    # than after 30 ms), so the default warm-up is 50 steps (about 15 ms).
     for i in range(args.warmup):
         run_prefill(i)
         run_decode(i)
