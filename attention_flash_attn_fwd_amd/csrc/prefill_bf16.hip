@@ -447,14 +447,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
   };
   // block skip: this wave's vote on key tile t (are all 32 of its rows
-  // negligible?), published in LDS; the other wave of the 64-row tile runs
-  // the same phase, so its vote on t arrives within a few instructions (the
-  // wait is bounded; past the bound the tile is kept).  One wave of the pair
-  // records the decisions on its live tiles; its bitmap store is a
-  // vector-memory operation that the phase's copy wait has to count.  True
-  // if tile t is skipped.
+  // negligible?), published in LDS.  The other wave of the 64-row tile runs
+  // the same phase, so its vote on t arrives within a few instructions;
+  // vote_collect waits for it (bounded; past the bound the tile is kept).
+  // The copy issue sits between the two, hiding the LDS round trip.  One
+  // wave of the pair records the decisions on its live tiles; its bitmap
+  // store is a vector-memory operation that the phase's copy wait has to
+  // count.  vote_collect is true if tile t is skipped.
   const bool records = SKIP && ((slot / p.gw) & 1) == 0;
-  auto vote_pair = [&](int t, float tmx_t) -> bool {
+  auto vote_publish = [&](int t, float tmx_t) -> bool {
     bool neg = true;
     if (t < wave_tiles)
       neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < p.thr) ||
@@ -463,6 +464,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
     if (lane == 0)
       __hip_atomic_store(&vote_lds[t & 1][wave], (t << 1) | (all_neg ? 1 : 0), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    return all_neg;
+  };
+  auto vote_collect = [&](int t, bool all_neg) -> bool {
     int other = -1;
     for (int spin = 0; spin < (1 << 16); ++spin) {
       other = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
@@ -550,27 +554,56 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
       if (2 < n_tiles) issue(2);
       block_barrier();
     }
-    for (int j = 0; j <= n_tiles; ++j) {
+    // wait for the copies before the newest, with this phase's bitmap store
+    // (issued after them) left in flight as well
+    const bool stores = records && p.skip_map;
+    auto wait_copies_voted = [&]() {
+      if (!stores) wait_all_but_newest();
+      else if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 1>();
+      else wait_vmem<DMA_HI + 1>();
+    };
+    auto general = [&](int j) {
       if (j >= 1 && j - 1 < wave_tiles && !skip_prev) pv(j - 1, pk);
       if (j < wave_tiles) qk(j, sc);
       block_barrier();
       const bool issues = j + 2 + grp < n_tiles;
+      float tmx = -INFINITY;
+      bool mine = false;
+      if (j < n_tiles) {
+        if (j < wave_tiles) tmx = row_max(j, sc);
+        mine = vote_publish(j, tmx);
+      }
       if (issues) issue(j + 2 + grp);
       if (j < n_tiles) {
-        const float tmx = j < wave_tiles ? row_max(j, sc) : -INFINITY;
-        const bool sk = vote_pair(j, tmx);
+        const bool sk = vote_collect(j, mine);
         m_true = fmaxf(m_true, tmx);
         if (j < wave_tiles && !sk) softmax(sc, tmx, pk);
         skip_prev = sk;
       }
-      // a bitmap store made in this phase follows the copies just issued
-      const bool stored = records && p.skip_map && j < wave_tiles;
       if (!issues) wait_vmem<0>();
-      else if (!stored) wait_all_but_newest();
-      else if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 1>();
-      else wait_vmem<DMA_HI + 1>();
+      else if (j < wave_tiles) wait_copies_voted();  // a bitmap store was made
+      else wait_all_but_newest();
+      block_barrier();
+    };
+    general(0);
+    // steady iterations: every step present, no mask (as in the dense loop)
+    const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
+    int j = 1;
+    for (; j < j_ss; ++j) {
+      if (!skip_prev) pv(j - 1, pk);
+      qk(j, sc);
+      block_barrier();
+      const float tmx = tile_max(sc);
+      const bool mine = vote_publish(j, tmx);
+      issue(j + 2 + grp);
+      const bool sk = vote_collect(j, mine);
+      m_true = fmaxf(m_true, tmx);
+      if (!sk) softmax(sc, tmx, pk);
+      skip_prev = sk;
+      wait_copies_voted();
       block_barrier();
     }
+    for (; j <= n_tiles; ++j) general(j);
     if (grp == 0) block_barrier();
   }
 
