@@ -613,20 +613,35 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = ln(sum) = (m + log2 l) ln 2
   if (!has_rows) return;
   const float lt = half_swap_add(l);
-  const int row = q0 + n;
-  if (row >= Sq) return;
   const float inv = 1.f / lt;
-  uint16_t* orow = p.o + qrow_off(row);
+  // The accumulator gives each lane 8-byte pieces of one row, so direct
+  // stores would write 16 bytes per row per instruction.  The wave's 32 x D
+  // tile goes through a private slice of the ring instead (every wave is past
+  // its last ring read here: a wave of group 0 reaches this point after the
+  // barrier that follows group 1's last P.V) and leaves as whole rows, 16
+  // bytes per lane.  The 16-byte chunk c of row r sits at chunk c ^ (r % CPR)
+  // of the slice row, which spreads a column of chunks over the banks.
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;     // rows per wave-wide store
+  static_assert(kWaves * 32 * D * 2 <= T::NST * T::STAGE, "output slices must fit in the ring");
+  LDS_AS unsigned char* ost = smem + wave * (32 * D * 2);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = db * 32 + g4 * 8 + hf * 4;
-      u32x2 w = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
-                 pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + d0) = w;
+      const u32x2 w = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
+                       pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
+      const int c = (db * 4 + g4) ^ (n % CPR);
+      *reinterpret_cast<LDS_AS u32x2*>(ost + n * (D * 2) + c * 16 + hf * 8) = w;
     }
-  if (hf == 0 && p.lse)
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 w = *reinterpret_cast<const LDS_AS u32x4*>(ost + r * (D * 2) + (c ^ (r % CPR)) * 16);
+    if (q0 + r < Sq) *reinterpret_cast<u32x4*>(p.o + qrow_off(q0 + r) + c * 8) = w;
+  }
+  const int row = q0 + n;
+  if (hf == 0 && row < Sq && p.lse)
     p.lse[PAGED ? (size_t)(qstart + row) * p.Hq + head : qbase + row] = (m_used + __log2f(lt)) * kLn2;
 }
 
