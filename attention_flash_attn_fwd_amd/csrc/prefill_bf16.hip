@@ -73,6 +73,8 @@ struct Params {
   const int32_t* seq_k;    // [N] cached tokens per sequence (Sk)
   const int32_t* table;    // [N, max_blocks] block table
   int N, max_blocks, num_blocks;
+  // work items (query block x head group) and how many each workgroup runs
+  int n_items, items_per_wg;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -152,11 +154,28 @@ struct Tile {
 #define LDS_AS __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// The kernel's argument block behind a pointer the compiler cannot see
+// through: the parameters are read through it once per work item, so they
+// live for that item only (an item loop would otherwise hold every parameter
+// in scalar registers across all items, and they would spill).
+constexpr int kComputeUnits = 256;  // MI355X
+// buffer resource word 3 for raw 32-bit accesses (data format 32)
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ const Params& item_params() {
+  auto ptr = (const __attribute__((address_space(4))) Params*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ptr));
+  return *(const Params*)ptr;
+}
+
 template <int D, bool CAUSAL, bool SKIP, bool PAGED>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
   using T = Tile<D>;
   constexpr int NKS = D / 16;  // 16-dim k-steps of Q.K^T
   constexpr int NDB = D / 32;  // 32-dim output blocks of P.V
+  constexpr int CPR = D / 8;   // 16-byte chunks per row of O
+  constexpr int RPI = 64 / CPR;  // rows per wave-wide store of O
+  constexpr int kOutStores = 32 / RPI + 1;  // store instructions per wave and item (O, LSE)
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
@@ -166,483 +185,571 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hf = lane >> 5;
 
-  // ---- work item: heaviest query blocks first (paged: across sequences)
-  const int bid = blockIdx.x;
-  const int hg = bid % p.n_hgrp;
-  const int seq = PAGED ? (bid / p.n_hgrp) % p.N : 0;
-  const int qblk = p.n_qblk - 1 - (PAGED ? bid / p.n_hgrp / p.N : bid / p.n_hgrp);
-  const int sub = hg % p.sub_per_kv;
-  const int bk = hg / p.sub_per_kv;
-  const int kvh = bk % p.Hkv, b = bk / p.Hkv;
-  // Waves w and w+4 share a SIMD and run the tile loop half an iteration
-  // apart (see below), so they get adjacent 32-row slots: equal causal tile
-  // counts keep both busy to the end.  With block skip, the two waves of a
-  // 64-row skip tile (slots s and s ^ gw) must run in the same half; this
-  // mapping gives that for gw >= 2, and slot = wave (pairing waves 2k and
-  // 2k+1) for gw == 1.
-  const int slot = (SKIP && p.gw == 1) ? wave : ((wave & 3) << 1) | (wave >> 2);
-  const int pslot = slot ^ p.gw;  // block skip: the other half of this skip tile
-  const int pwave = (SKIP && p.gw == 1) ? pslot : ((pslot & 1) << 2) | (pslot >> 1);
-  const int head = kvh * p.G + sub * p.gw + (slot % p.gw);
-  const int row0 = qblk * p.rows_per_wg;
-  const int q0 = row0 + (slot / p.gw) * 32;
-  // Sq query rows at key positions off .. off+Sq-1 of Sk keys (dense: all S)
-  int Sq = p.S, Sk = p.S, off = 0, qstart = 0;
-  if constexpr (PAGED) {
-    qstart = p.cu_q[seq];
-    Sq = p.cu_q[seq + 1] - qstart;
-    Sk = p.seq_k[seq];
-    off = Sk - Sq;
-    if (row0 >= Sq) return;  // whole workgroup past this chunk
-    if (Sq < 0 || off < 0 || Sk > p.max_blocks * 16) {
-      // lengths that do not fit the table: NaN rows, nothing read
-      const int row = q0 + n;
-      if (row < Sq) {
-        uint16_t* orow = p.o + ((size_t)(qstart + row) * p.Hq + head) * D;
-        for (int d = hf * 4; d < D; d += 8)
-          *reinterpret_cast<u32x2*>(orow + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-        if (hf == 0 && p.lse) p.lse[(size_t)(qstart + row) * p.Hq + head] = NAN;
-      }
-      return;
-    }
-  }
-  const int S = Sk;  // key count
-
-  const int wg_last = min(Sq, row0 + p.rows_per_wg) - 1;
-  const int n_tiles = CAUSAL ? (off + wg_last) / BN + 1 : (S + BN - 1) / BN;
-  const bool has_rows = q0 < Sq;
-  const int wave_tiles = !has_rows ? 0 : (CAUSAL ? (off + min(Sq - 1, q0 + 31)) / BN + 1 : n_tiles);
-
-  const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
-  const uint16_t* Kg = p.k + kvbase;
-  const uint16_t* Vg = p.v + kvbase;
-
-  // ---- asynchronous global -> LDS copy of tile t into stage t % NST.
-  // One wave-wide load fills 1 KiB of LDS (16 bytes per lane, in lane
-  // order); the lane fetches the global chunk that the padded layout puts
-  // there.  The NBLK blocks of a stage (K blocks 0 .. KSL-1, then V blocks)
-  // are numbered jointly and dealt round robin, block w + 8j to wave w, so
-  // every wave issues DMA_LO or DMA_HI of them; since the K tile is exactly
-  // KSL KiB, block i always lands at byte i KiB of the stage.  Slot g of a
-  // block is row g / SL, chunk g % SL (a pad slot re-reads chunk 0 of its
-  // row).  The per-lane source offsets are fixed for every tile: the tile's
-  // first key enters through the scalar base address.  Keys past the end
-  // are clamped to the last key and masked later.
-  constexpr int NBLK = T::KSL + T::VSL;
-  constexpr int DMA_HI = (NBLK + kWaves - 1) / kWaves, DMA_LO = NBLK / kWaves;
-  const bool dma_hi = wave < NBLK % kWaves;
-  uint32_t doff[DMA_HI];  // row * RB + chunk offset
-  int drow[DMA_HI];
-#pragma unroll
-  for (int j = 0; j < DMA_HI; ++j) {
-    const int i = wave + j * kWaves;
-    const bool is_k = i < T::KSL;
-    const int sl = is_k ? T::KSL : T::VSL;
-    const int g = (is_k ? i : i - T::KSL) * 64 + lane, c = g % sl;
-    drow[j] = g / sl;
-    doff[j] = (uint32_t)drow[j] * T::RB + (c < T::CH ? c : 0) * 16;
-  }
-  auto issue = [&](int t) {
-    const uint32_t st = smem_base + (t % T::NST) * T::STAGE;
-    const int key0 = t * BN;
-    const bool ragged = key0 + BN > S;  // clamp keys past the end to the last key
+  // ---- work items.  Workgroup g of G runs items g, 2G-1-g, 2G+g, 4G-1-g,
+  // ... (items_per_wg of them, those below n_items).  Items are numbered
+  // heaviest query block first, so each pair holds a heavy and a light
+  // block and the workgroups of a causal launch get equal tile counts.  An
+  // item's last phase issues the next item's Q and first two tiles, and its
+  // output stores drain while the next item starts.  The tile stages run on
+  // as one ring across items (ring = stage of the item's tile 0).
+  const int nwg = gridDim.x;
+  auto item_bid = [&](int it) {
+    return (it >> 1) * 2 * nwg + ((it & 1) ? 2 * nwg - 1 - (int)blockIdx.x : (int)blockIdx.x);
+  };
+  const int grp = wave >> 2;  // wave group of the ping-pong (see the tile loop)
+  bf16x8 qf[NKS];           // Q fragments (B operand): query q0+n, dims ks*16 + hf*8 .. +7
+  bool prefetched = false;  // Q and tiles 0, 1 of this item were issued by the previous one
+  int ring = 0;
+  for (int it = 0;; ++it) {
+    const Params& p = item_params();
+    const int bid = item_bid(it);
+    // ---- work item: heaviest query blocks first (paged: across sequences)
+    const int hg = bid % p.n_hgrp;
+    const int seq = PAGED ? (bid / p.n_hgrp) % p.N : 0;
+    const int qblk = p.n_qblk - 1 - (PAGED ? bid / p.n_hgrp / p.N : bid / p.n_hgrp);
+    const int sub = hg % p.sub_per_kv;
+    const int bk = hg / p.sub_per_kv;
+    const int kvh = bk % p.Hkv, b = bk / p.Hkv;
+    // Waves w and w+4 share a SIMD and run the tile loop half an iteration
+    // apart (see below), so they get adjacent 32-row slots: equal causal tile
+    // counts keep both busy to the end.  With block skip, the two waves of a
+    // 64-row skip tile (slots s and s ^ gw) must run in the same half; this
+    // mapping gives that for gw >= 2, and slot = wave (pairing waves 2k and
+    // 2k+1) for gw == 1.
+    const int slot = (SKIP && p.gw == 1) ? wave : ((wave & 3) << 1) | (wave >> 2);
+    const int pslot = slot ^ p.gw;  // block skip: the other half of this skip tile
+    const int pwave = (SKIP && p.gw == 1) ? pslot : ((pslot & 1) << 2) | (pslot >> 1);
+    const int head = kvh * p.G + sub * p.gw + (slot % p.gw);
+    const int row0 = qblk * p.rows_per_wg;
+    const int q0 = row0 + (slot / p.gw) * 32;
+    // Sq query rows at key positions off .. off+Sq-1 of Sk keys (dense: all S)
+    int Sq = p.S, Sk = p.S, off = 0, qstart = 0;
     if constexpr (PAGED) {
-      // the tile's 4 pool blocks (table entries clamped into the pool)
-      const int32_t* trow = p.table + (size_t)seq * p.max_blocks;
-      const int nbs = (S + 15) >> 4;
-      int e[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int idx = t * 4 + x;
-        const int v = idx < nbs ? trow[idx] : 0;
-        e[x] = min(max(v, 0), p.num_blocks - 1);
+      qstart = p.cu_q[seq];
+      Sq = p.cu_q[seq + 1] - qstart;
+      Sk = p.seq_k[seq];
+      off = Sk - Sq;
+      if (row0 >= Sq) return;  // whole workgroup past this chunk
+      if (Sq < 0 || off < 0 || Sk > p.max_blocks * 16) {
+        // lengths that do not fit the table: NaN rows, nothing read
+        const int row = q0 + n;
+        if (row < Sq) {
+          uint16_t* orow = p.o + ((size_t)(qstart + row) * p.Hq + head) * D;
+          for (int d = hf * 4; d < D; d += 8)
+            *reinterpret_cast<u32x2*>(orow + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+          if (hf == 0 && p.lse) p.lse[(size_t)(qstart + row) * p.Hq + head] = NAN;
+        }
+        return;
       }
-      const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k);
-      const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v);
-#pragma unroll
-      for (int j = 0; j < DMA_HI; ++j) {
-        const int i = wave + j * kWaves;
-        if (j == DMA_LO && !dma_hi) break;
-        const int r = drow[j];
-        const int key = key0 + min(r, S - 1 - key0);
-        const int bl = (key >> 4) - t * 4;
-        const int ph = bl == 0 ? e[0] : bl == 1 ? e[1] : bl == 2 ? e[2] : e[3];
-        const uint32_t choff = doff[j] - (uint32_t)r * T::RB;
-        const unsigned char* pool = i < T::KSL ? kpool : vpool;
-        dma16_va(pool + ((((size_t)ph * p.Hkv + kvh) << 4) + (key & 15)) * T::RB + choff,
-                 st + i * 1024);
-      }
-      return;
     }
-    const uint16_t* kb_ = Kg + (size_t)key0 * D;
-    const uint16_t* vb_ = Vg + (size_t)key0 * D;
-    if (!ragged) {
+    const int S = Sk;  // key count
+
+    const int wg_last = min(Sq, row0 + p.rows_per_wg) - 1;
+    const int n_tiles = CAUSAL ? (off + wg_last) / BN + 1 : (S + BN - 1) / BN;
+    const bool has_rows = q0 < Sq;
+    const int wave_tiles = !has_rows ? 0 : (CAUSAL ? (off + min(Sq - 1, q0 + 31)) / BN + 1 : n_tiles);
+    // whether the workgroup has a next item (dense prefill only)
+    auto has_next = [&]() {
+      return !PAGED && !SKIP && it + 1 < p.items_per_wg && item_bid(it + 1) < p.n_items;
+    };
+
+    const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
+    const uint16_t* Kg = p.k + kvbase;
+    const uint16_t* Vg = p.v + kvbase;
+
+    // ---- asynchronous global -> LDS copy of tile t into stage t % NST.
+    // One wave-wide load fills 1 KiB of LDS (16 bytes per lane, in lane
+    // order); the lane fetches the global chunk that the padded layout puts
+    // there.  The NBLK blocks of a stage (K blocks 0 .. KSL-1, then V blocks)
+    // are numbered jointly and dealt round robin, block w + 8j to wave w, so
+    // every wave issues DMA_LO or DMA_HI of them; since the K tile is exactly
+    // KSL KiB, block i always lands at byte i KiB of the stage.  Slot g of a
+    // block is row g / SL, chunk g % SL (a pad slot re-reads chunk 0 of its
+    // row).  The per-lane source offsets are fixed for every tile: the tile's
+    // first key enters through the scalar base address.  Keys past the end
+    // are clamped to the last key and masked later.
+    constexpr int NBLK = T::KSL + T::VSL;
+    constexpr int DMA_HI = (NBLK + kWaves - 1) / kWaves, DMA_LO = NBLK / kWaves;
+    const bool dma_hi = wave < NBLK % kWaves;
+    uint32_t doff[DMA_HI];  // row * RB + chunk offset
+    int drow[DMA_HI];
 #pragma unroll
-      for (int j = 0; j < DMA_HI; ++j) {
-        const int i = wave + j * kWaves;
-        if (j == DMA_LO && !dma_hi) break;
-        dma16(i < T::KSL ? kb_ : vb_, doff[j], st + i * 1024);
+    for (int j = 0; j < DMA_HI; ++j) {
+      const int i = wave + j * kWaves;
+      const bool is_k = i < T::KSL;
+      const int sl = is_k ? T::KSL : T::VSL;
+      const int g = (is_k ? i : i - T::KSL) * 64 + lane, c = g % sl;
+      drow[j] = g / sl;
+      doff[j] = (uint32_t)drow[j] * T::RB + (c < T::CH ? c : 0) * 16;
+    }
+    // Dense tile t of the item whose K and V start at kg and vg, into stage
+    // (t + rg) % NST.
+    auto issue_dense = [&](const uint16_t* kg, const uint16_t* vg, int t, int rg) {
+      const uint32_t st = smem_base + ((t + rg) % T::NST) * T::STAGE;
+      const int key0 = t * BN;
+      const uint16_t* kb_ = kg + (size_t)key0 * D;
+      const uint16_t* vb_ = vg + (size_t)key0 * D;
+      if (key0 + BN <= S) {
+#pragma unroll
+        for (int j = 0; j < DMA_HI; ++j) {
+          const int i = wave + j * kWaves;
+          if (j == DMA_LO && !dma_hi) break;
+          dma16(i < T::KSL ? kb_ : vb_, doff[j], st + i * 1024);
+        }
+      } else {
+        const int lim = S - 1 - key0;  // clamp keys past the end to the last key
+#pragma unroll
+        for (int j = 0; j < DMA_HI; ++j) {
+          const int i = wave + j * kWaves;
+          if (j == DMA_LO && !dma_hi) break;
+          const uint32_t o = doff[j] - (uint32_t)(drow[j] - min(drow[j], lim)) * T::RB;
+          dma16(i < T::KSL ? kb_ : vb_, o, st + i * 1024);
+        }
       }
+    };
+    auto issue = [&](int t) {
+      if constexpr (PAGED) {
+        const uint32_t st = smem_base + ((t + ring) % T::NST) * T::STAGE;
+        const int key0 = t * BN;
+        // the tile's 4 pool blocks (table entries clamped into the pool)
+        const int32_t* trow = p.table + (size_t)seq * p.max_blocks;
+        const int nbs = (S + 15) >> 4;
+        int e[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int idx = t * 4 + x;
+          const int v = idx < nbs ? trow[idx] : 0;
+          e[x] = min(max(v, 0), p.num_blocks - 1);
+        }
+        const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k);
+        const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v);
+#pragma unroll
+        for (int j = 0; j < DMA_HI; ++j) {
+          const int i = wave + j * kWaves;
+          if (j == DMA_LO && !dma_hi) break;
+          const int r = drow[j];
+          const int key = key0 + min(r, S - 1 - key0);
+          const int bl = (key >> 4) - t * 4;
+          const int ph = bl == 0 ? e[0] : bl == 1 ? e[1] : bl == 2 ? e[2] : e[3];
+          const uint32_t choff = doff[j] - (uint32_t)r * T::RB;
+          const unsigned char* pool = i < T::KSL ? kpool : vpool;
+          dma16_va(pool + ((((size_t)ph * p.Hkv + kvh) << 4) + (key & 15)) * T::RB + choff,
+                   st + i * 1024);
+        }
+      } else {
+        issue_dense(Kg, Vg, t, ring);
+      }
+    };
+    // wait until only the DMA blocks of the newest tile are in flight
+    auto wait_all_but_newest = [&]() {
+      if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO>(); else wait_vmem<DMA_HI>();
+    };
+
+    // ---- Q fragment (B operand): query q0+n, dims ks*16 + hf*8 .. +7
+    const size_t qbase = ((size_t)b * p.Hq + head) * Sq;
+    // element offset of query row r (dense [B,Hq,S,D]; paged packed [total_q,Hq,D])
+    auto qrow_off = [&](int r) -> size_t {
+      return PAGED ? ((size_t)(qstart + r) * p.Hq + head) * D : (qbase + r) * D;
+    };
+    if (!prefetched) {
+      const int qrow = min(q0 + n, Sq - 1);
+      const uint16_t* qp = p.q + qrow_off(qrow) + hf * 8;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      // The first two tile copies go out together with the Q loads; then one
+      // wait the compiler can see (vmcnt(0)) completes all of them, so it
+      // places no vector-memory waits of its own inside the loop, where they
+      // would also drain the tile prefetches.
+      issue(0);
+      if (n_tiles > 1) issue(1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
-      const int lim = S - 1 - key0;
+      // Q (in this wave's output slice of the previous item) and tiles 0 and
+      // 1 were copied by the previous item, ahead of its output stores, which
+      // may still be in flight
+      wait_vmem<kOutStores>();
+      const LDS_AS unsigned char* qs =
+          smem + ((ring + 2 + grp) % T::NST) * T::STAGE + (wave & 3) * (32 * D * 2);
 #pragma unroll
-      for (int j = 0; j < DMA_HI; ++j) {
-        const int i = wave + j * kWaves;
-        if (j == DMA_LO && !dma_hi) break;
-        const uint32_t o = doff[j] - (uint32_t)(drow[j] - min(drow[j], lim)) * T::RB;
-        dma16(i < T::KSL ? kb_ : vb_, o, st + i * 1024);
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[ks] = *reinterpret_cast<const LDS_AS bf16x8*>(qs + (n * CPR + ((2 * ks + hf) ^ (n % CPR))) * 16);
+      // read before tile 2 or 3 of this item can land in the slice
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+
+    // per-lane LDS offsets of the MFMA operand reads (see Tile)
+    const int k_base = n * T::RK + hf * 16;                 // + kb*32*RK + ks*32
+    const int vg = lane >> 4, vs = lane & 15;
+    const int v_base = ((vg >> 1) * 4 + (vs >> 2)) * T::RV + ((vg & 1) * 16 + 4 * (vs & 3)) * 2;
+
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    float m_used = kUnset;   // reference max of the exponentials (log2 units)
+    float m_true = kUnset;   // running max over the tiles before the current one
+    float l = 0.f;
+    unsigned skipped = 0;
+    const float sl2 = p.sl2;
+    const int first_masked = CAUSAL ? min((off + q0) / BN, S / BN) : S / BN;
+
+    // S^T of key tile t (raw scores) = K Q^T: two independent 32-key
+    // accumulator chains, operand reads running ahead of the MFMAs
+    auto qk = [&](int t, f32x16* sc) {
+      const LDS_AS unsigned char* kp = smem + ((t + ring) % T::NST) * T::STAGE + k_base;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[0][i] = sc[1][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + ks * 32);
+        const bf16x8 a1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK + ks * 32);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sc[0], 0, 0, 0);
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], sc[1], 0, 0, 0);
       }
-    }
-  };
-  // wait until only the DMA blocks of the newest tile are in flight
-  auto wait_all_but_newest = [&]() {
-    if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO>(); else wait_vmem<DMA_HI>();
-  };
-
-  // ---- Q fragment (B operand): query q0+n, dims ks*16 + hf*8 .. +7
-  const size_t qbase = ((size_t)b * p.Hq + head) * Sq;
-  // element offset of query row r (dense [B,Hq,S,D]; paged packed [total_q,Hq,D])
-  auto qrow_off = [&](int r) -> size_t {
-    return PAGED ? ((size_t)(qstart + r) * p.Hq + head) * D : (qbase + r) * D;
-  };
-  bf16x8 qf[NKS];
-  {
-    const int qrow = min(q0 + n, Sq - 1);
-    const uint16_t* qp = p.q + qrow_off(qrow) + hf * 8;
+      // 4 operand reads ahead, then alternate MFMA / read
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-  }
-  // The first two tile copies go out together with the Q loads; then one
-  // wait the compiler can see (vmcnt(0)) completes all of them, so it
-  // places no vector-memory waits of its own inside the loop, where they
-  // would also drain the tile prefetches.
-  issue(0);
-  if (n_tiles > 1) issue(1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-
-  // per-lane LDS offsets of the MFMA operand reads (see Tile)
-  const int k_base = n * T::RK + hf * 16;                 // + kb*32*RK + ks*32
-  const int vg = lane >> 4, vs = lane & 15;
-  const int v_base = ((vg >> 1) * 4 + (vs >> 2)) * T::RV + ((vg & 1) * 16 + 4 * (vs & 3)) * 2;
-
-  f32x16 acc[NDB];
+      for (int i = 0; i < 2 * NKS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // mask (diagonal and ragged tiles only) and scaled row max of a score tile
+    auto mask_tile = [&](int t, f32x16* sc) {
+      if (t >= first_masked) {
+        const int c0 = t * BN, qi = q0 + n;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  float m_used = kUnset;   // reference max of the exponentials (log2 units)
-  float m_true = kUnset;   // running max over the tiles before the current one
-  float l = 0.f;
-  unsigned skipped = 0;
-  const float sl2 = p.sl2;
-  const int first_masked = CAUSAL ? min((off + q0) / BN, S / BN) : S / BN;
-
-  // S^T of key tile t (raw scores) = K Q^T: two independent 32-key
-  // accumulator chains, operand reads running ahead of the MFMAs
-  auto qk = [&](int t, f32x16* sc) {
-    const LDS_AS unsigned char* kp = smem + (t % T::NST) * T::STAGE + k_base;
+          for (int i = 0; i < 16; ++i) {
+            const int key = c0 + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+            if (key >= S || (CAUSAL && key > off + qi)) sc[kb][i] = -INFINITY;
+          }
+      }
+    };
+    auto tile_max = [&](const f32x16* sc) -> float {
+      float m0 = fmaxf(sc[0][0], sc[1][0]), m1 = fmaxf(sc[0][1], sc[1][1]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[0][i] = sc[1][i] = 0.f;
+      for (int i = 2; i < 16; i += 2) {
+        m0 = fmaxf(fmaxf(m0, sc[0][i]), sc[1][i]);
+        m1 = fmaxf(fmaxf(m1, sc[0][i + 1]), sc[1][i + 1]);
+      }
+      return half_swap_max(fmaxf(m0, m1)) * sl2;
+    };
+    auto row_max = [&](int t, f32x16* sc) -> float {
+      mask_tile(t, sc);
+      return tile_max(sc);
+    };
+    // softmax of a score tile into bf16 P (packed for the P.V MFMA).  The
+    // exponent reference moves (with a rescale of O and l) only when the row
+    // max grew by more than 8, a factor 256; the result is exact after 1/l.
+    auto softmax = [&](f32x16* sc, float tmx, uint32_t (*pk)[8]) {
+      if (__any(tmx > m_used + 8.f)) {
+        const float m_new = fmaxf(m_used, tmx);
+        const float alpha = fast_exp2(m_used - m_new);
+        l *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + ks * 32);
-      const bf16x8 a1 = *reinterpret_cast<const LDS_AS bf16x8*>(kp + 32 * T::RK + ks * 32);
-      sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sc[0], 0, 0, 0);
-      sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], sc[1], 0, 0, 0);
-    }
-    // 4 operand reads ahead, then alternate MFMA / read
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 2 * NKS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  };
-  // mask (diagonal and ragged tiles only) and scaled row max of a score tile
-  auto mask_tile = [&](int t, f32x16* sc) {
-    if (t >= first_masked) {
-      const int c0 = t * BN, qi = q0 + n;
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        m_used = m_new;
+      }
+      const float nm = -m_used;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = c0 + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          if (key >= S || (CAUSAL && key > off + qi)) sc[kb][i] = -INFINITY;
-        }
-    }
-  };
-  auto tile_max = [&](const f32x16* sc) -> float {
-    float m0 = fmaxf(sc[0][0], sc[1][0]), m1 = fmaxf(sc[0][1], sc[1][1]);
+        for (int i = 0; i < 16; i += 2)
+          pk[kb][i >> 1] = pack_bf16(fast_exp2(fmaf(sc[kb][i], sl2, nm)),
+                                     fast_exp2(fmaf(sc[kb][i + 1], sl2, nm)));
+      // row sum of the bf16-rounded P (the values P.V uses), two per dot2
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-      m0 = fmaxf(fmaxf(m0, sc[0][i]), sc[1][i]);
-      m1 = fmaxf(fmaxf(m1, sc[0][i + 1]), sc[1][i + 1]);
-    }
-    return half_swap_max(fmaxf(m0, m1)) * sl2;
-  };
-  auto row_max = [&](int t, f32x16* sc) -> float {
-    mask_tile(t, sc);
-    return tile_max(sc);
-  };
-  // softmax of a score tile into bf16 P (packed for the P.V MFMA).  The
-  // exponent reference moves (with a rescale of O and l) only when the row
-  // max grew by more than 8, a factor 256; the result is exact after 1/l.
-  auto softmax = [&](f32x16* sc, float tmx, uint32_t (*pk)[8]) {
-    if (__any(tmx > m_used + 8.f)) {
-      const float m_new = fmaxf(m_used, tmx);
-      const float alpha = fast_exp2(m_used - m_new);
-      l *= alpha;
+      for (int j = 0; j < 8; ++j) {
+        rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[0][j]), kOnes2, rs0, false);
+        rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[1][j]), kOnes2, rs1, false);
+      }
+      l += rs0 + rs1;
+    };
+    // O^T += V^T P^T for key tile t; V^T fragments come from the transposing
+    // LDS read, running ahead of the MFMAs
+    auto pv = [&](int t, uint32_t (*pk)[8]) {
+      const LDS_AS unsigned char* vl = smem + ((t + ring) % T::NST) * T::STAGE + T::KT + v_base;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 pw = {pk[kb][kk * 4 + 0], pk[kb][kk * 4 + 1], pk[kb][kk * 4 + 2],
+                            pk[kb][kk * 4 + 3]};
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const LDS_AS unsigned char* va = vl + (kb * 32 + kk * 16) * T::RV + db * 64;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)va);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(va + 8 * T::RV));
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+          }
+        }
+      // three MFMAs' operands ahead, then alternate one MFMA / two reads
+      constexpr int NM = 4 * NDB;
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < NM - 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    };
+    // block skip: this wave's vote on key tile t (are all 32 of its rows
+    // negligible?), published in LDS.  The other wave of the 64-row tile runs
+    // the same phase, so its vote on t arrives within a few instructions;
+    // vote_collect waits for it (bounded; past the bound the tile is kept).
+    // The copy issue sits between the two, hiding the LDS round trip.  One
+    // wave of the pair records the decisions on its live tiles; its bitmap
+    // store is a vector-memory operation that the phase's copy wait has to
+    // count.  vote_collect is true if tile t is skipped.
+    const bool records = SKIP && ((slot / p.gw) & 1) == 0;
+    auto vote_publish = [&](int t, float tmx_t) -> bool {
+      bool neg = true;
+      if (t < wave_tiles)
+        neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < p.thr) ||
+              (q0 + n >= S);
+      const bool all_neg = __all(neg);
+      if (lane == 0)
+        __hip_atomic_store(&vote_lds[t & 1][wave], (t << 1) | (all_neg ? 1 : 0), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+      return all_neg;
+    };
+    auto vote_collect = [&](int t, bool all_neg) -> bool {
+      int other = -1;
+      for (int spin = 0; spin < (1 << 16); ++spin) {
+        other = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+            &vote_lds[t & 1][pwave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if ((other >> 1) == t) break;
+      }
+      const bool sk = all_neg && (other >> 1) == t && (other & 1);
+      if (records && t < wave_tiles) {
+        if (lane == 0 && p.skip_map)
+          p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = sk ? 1 : 0;
+        skipped += sk ? 1u : 0u;
+      }
+      return sk;
+    };
+
+    // The last phase pair of the item: P.V of its last tile, then a VALU
+    // phase with no tile work left, which takes the epilogue and, when the
+    // workgroup has a next item, that item's Q and first two tiles.
+    //  * O = acc / l (bf16, RNE) goes through a private LDS slice and leaves
+    //    as whole rows, 16 bytes per lane (the accumulator holds 8-byte pieces
+    //    of a row per lane).  Group 0's slices sit in the stage of tile n-2,
+    //    group 1's in that of tile n-1: nobody reads them any more when the
+    //    group gets here (group 1 reads tile n-1 during group 0's last VALU
+    //    phase, which is why group 0 does not use it).  Chunk c of row r sits
+    //    at chunk c ^ (r % CPR) of the slice row, spreading a column of chunks
+    //    over the banks.  LSE = ln(sum) = (m + log2 l) ln 2.
+    //  * The stores go through buffer resources that cover exactly this
+    //    wave's valid rows (the range check drops the rest), so every wave
+    //    issues kOutStores of them, as its last vector-memory operations of
+    //    the item; the next item's first wait leaves them in flight.
+    //  * Once the slice has been read back, the next item's Q rows land in it
+    //    by LDS copy (same swizzle), and its tiles 0 and 1 go to the two
+    //    stages after this item's last one (they held tiles n-4 and n-3).
+    auto finish = [&](bool do_pv, uint32_t (*pk)[8]) {
+      if (do_pv) pv(n_tiles - 1, pk);
+      block_barrier();
+      if (SKIP && lane == 0 && skipped && p.skip_count)
+        atomicAdd(p.skip_count, (unsigned long long)skipped);
+      const float lt = half_swap_add(l);
+      const float inv = 1.f / lt;
+      static_assert(4 * 32 * D * 2 <= T::STAGE, "four output slices must fit in a stage");
+      const uint32_t slice = ((ring + n_tiles + 2 + grp) % T::NST) * T::STAGE + (wave & 3) * (32 * D * 2);
+      LDS_AS unsigned char* ost = smem + slice;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m_used = m_new;
-    }
-    const float nm = -m_used;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2)
-        pk[kb][i >> 1] = pack_bf16(fast_exp2(fmaf(sc[kb][i], sl2, nm)),
-                                   fast_exp2(fmaf(sc[kb][i + 1], sl2, nm)));
-    // row sum of the bf16-rounded P (the values P.V uses), two per dot2
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[0][j]), kOnes2, rs0, false);
-      rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[1][j]), kOnes2, rs1, false);
-    }
-    l += rs0 + rs1;
-  };
-  // O^T += V^T P^T for key tile t; V^T fragments come from the transposing
-  // LDS read, running ahead of the MFMAs
-  auto pv = [&](int t, uint32_t (*pk)[8]) {
-    const LDS_AS unsigned char* vl = smem + (t % T::NST) * T::STAGE + T::KT + v_base;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const u32x4 pw = {pk[kb][kk * 4 + 0], pk[kb][kk * 4 + 1], pk[kb][kk * 4 + 2],
-                          pk[kb][kk * 4 + 3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const LDS_AS unsigned char* va = vl + (kb * 32 + kk * 16) * T::RV + db * 64;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)va);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(va + 8 * T::RV));
-          const bf16x8 a =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const u32x2 w = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
+                           pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
+          const int c = (db * 4 + g4) ^ (n % CPR);
+          *reinterpret_cast<LDS_AS u32x2*>(ost + n * (D * 2) + c * 16 + hf * 8) = w;
         }
-      }
-    // three MFMAs' operands ahead, then alternate one MFMA / two reads
-    constexpr int NM = 4 * NDB;
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      u32x4 ow[32 / RPI];
 #pragma unroll
-    for (int i = 0; i < NM - 3; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-  };
-  // block skip: this wave's vote on key tile t (are all 32 of its rows
-  // negligible?), published in LDS.  The other wave of the 64-row tile runs
-  // the same phase, so its vote on t arrives within a few instructions;
-  // vote_collect waits for it (bounded; past the bound the tile is kept).
-  // The copy issue sits between the two, hiding the LDS round trip.  One
-  // wave of the pair records the decisions on its live tiles; its bitmap
-  // store is a vector-memory operation that the phase's copy wait has to
-  // count.  vote_collect is true if tile t is skipped.
-  const bool records = SKIP && ((slot / p.gw) & 1) == 0;
-  auto vote_publish = [&](int t, float tmx_t) -> bool {
-    bool neg = true;
-    if (t < wave_tiles)
-      neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < p.thr) ||
-            (q0 + n >= S);
-    const bool all_neg = __all(neg);
-    if (lane == 0)
-      __hip_atomic_store(&vote_lds[t & 1][wave], (t << 1) | (all_neg ? 1 : 0), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_WORKGROUP);
-    return all_neg;
-  };
-  auto vote_collect = [&](int t, bool all_neg) -> bool {
-    int other = -1;
-    for (int spin = 0; spin < (1 << 16); ++spin) {
-      other = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-          &vote_lds[t & 1][pwave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-      if ((other >> 1) == t) break;
-    }
-    const bool sk = all_neg && (other >> 1) == t && (other & 1);
-    if (records && t < wave_tiles) {
-      if (lane == 0 && p.skip_map)
-        p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = sk ? 1 : 0;
-      skipped += sk ? 1u : 0u;
-    }
-    return sk;
-  };
-
-  f32x16 sc[2];
-  if constexpr (!SKIP) {
-    // Ping-pong.  Each wave alternates an MFMA phase (P.V of tile j-1, then
-    // Q.K^T of tile j) and a VALU phase (mask, row max and softmax of tile
-    // j), separated by workgroup barriers.  The second wave of each SIMD
-    // (waves 4-7, group 1) runs one barrier behind the first, so at every
-    // moment one wave of the pair feeds the matrix core while the other's
-    // exponentials run on the vector ALU; a wave that mixed both kinds of
-    // work in one stream would not overlap them.  Both groups run the same
-    // code, so the scores and P never need registers at the same time.
-    //
-    // DMA: group 0 issues its share of tile j+2 in its VALU phase j, group
-    // 1 its share of tile j+3 (and of tile 2 in its extra first slot); the
-    // issue stalls the issuing wave, and an MFMA-phase wave would hold the
-    // matrix core idle meanwhile.  The stage a share overwrites was last
-    // read before the preceding barrier.  At the end of its VALU phase j
-    // every wave waits until only the share it has just issued is in
-    // flight: group 0's share of tile j+1 is then complete at the barrier
-    // after which the first Q.K^T of tile j+1 starts, group 1's share of
-    // tile j+2 a half iteration before the corresponding barrier.
-    //
-    // The iterations in which every step is present (no causal mask, no
-    // pipeline start or end) run a copy of the body without the tests.
-    const int grp = wave >> 2;
-    uint32_t pk[2][8];
-    block_barrier();
-    if (grp == 1) {
-      if (2 < n_tiles) issue(2);
-      block_barrier();
-    }
-    auto general = [&](int j) {
-      if (j >= 1 && j - 1 < wave_tiles) pv(j - 1, pk);
-      if (j < wave_tiles) qk(j, sc);
-      block_barrier();
-      const bool issues = j + 2 + grp < n_tiles;
-      if (issues) issue(j + 2 + grp);
-      if (j < wave_tiles) softmax(sc, row_max(j, sc), pk);
-      if (issues) wait_all_but_newest(); else wait_vmem<0>();
-      block_barrier();
-    };
-    general(0);
-    const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
-    int j = 1;
-    for (; j < j_ss; ++j) {
-      pv(j - 1, pk);
-      qk(j, sc);
-      block_barrier();
-      issue(j + 2 + grp);
-      softmax(sc, tile_max(sc), pk);
-      wait_all_but_newest();
-      block_barrier();
-    }
-    for (; j <= n_tiles; ++j) general(j);
-    if (grp == 0) block_barrier();
-  } else {
-    // Block skip, in the same ping-pong.  In its VALU phase j a wave takes
-    // the row maxima of tile j, votes, and waits for the vote of the other
-    // wave of the 64-row tile (same group, same phase).  A skipped tile loses
-    // its softmax now and its P.V in the next MFMA phase; the running max of
-    // the decisions (m_true) takes every tile, skipped or not.
-    const int grp = wave >> 2;
-    uint32_t pk[2][8];
-    bool skip_prev = false;
-    if (lane == 0) {
-      vote_lds[0][wave] = -2;
-      vote_lds[1][wave] = -2;
-    }
-    block_barrier();
-    if (grp == 1) {
-      if (2 < n_tiles) issue(2);
-      block_barrier();
-    }
-    // wait for the copies before the newest, with this phase's bitmap store
-    // (issued after them) left in flight as well
-    const bool stores = records && p.skip_map;
-    auto wait_copies_voted = [&]() {
-      if (!stores) wait_all_but_newest();
-      else if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 1>();
-      else wait_vmem<DMA_HI + 1>();
-    };
-    auto general = [&](int j) {
-      if (j >= 1 && j - 1 < wave_tiles && !skip_prev) pv(j - 1, pk);
-      if (j < wave_tiles) qk(j, sc);
-      block_barrier();
-      const bool issues = j + 2 + grp < n_tiles;
-      float tmx = -INFINITY;
-      bool mine = false;
-      if (j < n_tiles) {
-        if (j < wave_tiles) tmx = row_max(j, sc);
-        mine = vote_publish(j, tmx);
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + lane / CPR, c = lane % CPR;
+        ow[i] = *reinterpret_cast<const LDS_AS u32x4*>(ost + r * (D * 2) + (c ^ (r % CPR)) * 16);
       }
-      if (issues) issue(j + 2 + grp);
-      if (j < n_tiles) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slice read back before it is refilled
+      if (has_next()) {
+        const int next_bid = item_bid(it + 1);
+        const int nhg = next_bid % p.n_hgrp;
+        const int nqblk = p.n_qblk - 1 - next_bid / p.n_hgrp;
+        const int nbk = nhg / p.sub_per_kv;
+        const int nkvh = nbk % p.Hkv, nb = nbk / p.Hkv;
+        const int nhead = nkvh * p.G + (nhg % p.sub_per_kv) * p.gw + (slot % p.gw);
+        const int nrow0 = nqblk * p.rows_per_wg;
+        const int nq0 = nrow0 + (slot / p.gw) * 32;
+        const int nn_tiles = CAUSAL ? (min(S, nrow0 + p.rows_per_wg) - 1) / BN + 1 : (S + BN - 1) / BN;
+        const uint16_t* nqh = p.q + ((size_t)nb * p.Hq + nhead) * (size_t)S * D;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int sl = i * 64 + lane, r = sl / CPR, c = (sl % CPR) ^ (r % CPR);
+          dma16(nqh, (uint32_t)(min(nq0 + r, S - 1) * (D * 2) + c * 16), smem_base + slice + i * 1024);
+        }
+        const size_t nkv = ((size_t)nb * p.Hkv + nkvh) * (size_t)S * D;
+        issue_dense(p.k + nkv, p.v + nkv, 0, ring + n_tiles);
+        if (nn_tiles > 1) issue_dense(p.k + nkv, p.v + nkv, 1, ring + n_tiles);
+      }
+      const int nvalid = has_rows ? min(32, Sq - q0) : 0;
+      const int ostride = (PAGED ? p.Hq : 1) * D * 2;  // bytes from one row of O to the next
+      const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          p.o + (has_rows ? qrow_off(q0) : 0), (short)0,
+          nvalid > 0 ? (nvalid - 1) * ostride + D * 2 : 0, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(ow[i], orsrc, (i * RPI + lane / CPR) * ostride + (lane % CPR) * 16, 0, 0);
+      const int lstride = (PAGED ? p.Hq : 1) * 4;
+      float* lrow0 = p.lse == nullptr || !has_rows
+                         ? p.lse
+                         : p.lse + (PAGED ? (size_t)(qstart + q0) * p.Hq + head : qbase + q0);
+      const auto lrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          lrow0, (short)0, (p.lse != nullptr && nvalid > 0) ? (nvalid - 1) * lstride + 4 : 0, kBufferFlags);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m_used + __log2f(lt)) * kLn2), lrsrc,
+                                            n * lstride, 0, 0);  // both halves hold the same value
+      block_barrier();
+      if (grp == 0) block_barrier();
+    };
+
+    f32x16 sc[2];
+    if constexpr (!SKIP) {
+      // Ping-pong.  Each wave alternates an MFMA phase (P.V of tile j-1, then
+      // Q.K^T of tile j) and a VALU phase (mask, row max and softmax of tile
+      // j), separated by workgroup barriers.  The second wave of each SIMD
+      // (waves 4-7, group 1) runs one barrier behind the first, so at every
+      // moment one wave of the pair feeds the matrix core while the other's
+      // exponentials run on the vector ALU; a wave that mixed both kinds of
+      // work in one stream would not overlap them.  Both groups run the same
+      // code, so the scores and P never need registers at the same time.
+      //
+      // DMA: group 0 issues its share of tile j+2 in its VALU phase j, group
+      // 1 its share of tile j+3 (and of tile 2 in its extra first slot); the
+      // issue stalls the issuing wave, and an MFMA-phase wave would hold the
+      // matrix core idle meanwhile.  The stage a share overwrites was last
+      // read before the preceding barrier.  At the end of its VALU phase j
+      // every wave waits until only the share it has just issued is in
+      // flight: group 0's share of tile j+1 is then complete at the barrier
+      // after which the first Q.K^T of tile j+1 starts, group 1's share of
+      // tile j+2 a half iteration before the corresponding barrier.
+      //
+      // The iterations in which every step is present (no causal mask, no
+      // pipeline start or end) run a copy of the body without the tests.
+      uint32_t pk[2][8];
+      block_barrier();
+      if (grp == 1) {
+        if (2 < n_tiles) issue(2);
+        block_barrier();
+      }
+      auto general = [&](int j) {
+        if (j >= 1 && j - 1 < wave_tiles) pv(j - 1, pk);
+        if (j < wave_tiles) qk(j, sc);
+        block_barrier();
+        const bool issues = j + 2 + grp < n_tiles;
+        if (issues) issue(j + 2 + grp);
+        if (j < wave_tiles) softmax(sc, row_max(j, sc), pk);
+        if (issues) wait_all_but_newest(); else wait_vmem<0>();
+        block_barrier();
+      };
+      general(0);
+      const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
+      int j = 1;
+      for (; j < j_ss; ++j) {
+        pv(j - 1, pk);
+        qk(j, sc);
+        block_barrier();
+        issue(j + 2 + grp);
+        softmax(sc, tile_max(sc), pk);
+        wait_all_but_newest();
+        block_barrier();
+      }
+      for (; j < n_tiles; ++j) general(j);
+      finish(n_tiles - 1 < wave_tiles, pk);
+    } else {
+      // Block skip, in the same ping-pong.  In its VALU phase j a wave takes
+      // the row maxima of tile j, votes, and waits for the vote of the other
+      // wave of the 64-row tile (same group, same phase).  A skipped tile loses
+      // its softmax now and its P.V in the next MFMA phase; the running max of
+      // the decisions (m_true) takes every tile, skipped or not.
+      uint32_t pk[2][8];
+      bool skip_prev = false;
+      if (lane == 0) {
+        vote_lds[0][wave] = -2;
+        vote_lds[1][wave] = -2;
+      }
+      block_barrier();
+      if (grp == 1) {
+        if (2 < n_tiles) issue(2);
+        block_barrier();
+      }
+      // wait for the copies before the newest, with this phase's bitmap store
+      // (issued after them) left in flight as well
+      const bool stores = records && p.skip_map;
+      auto wait_copies_voted = [&]() {
+        if (!stores) wait_all_but_newest();
+        else if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 1>();
+        else wait_vmem<DMA_HI + 1>();
+      };
+      auto general = [&](int j) {
+        if (j >= 1 && j - 1 < wave_tiles && !skip_prev) pv(j - 1, pk);
+        if (j < wave_tiles) qk(j, sc);
+        block_barrier();
+        const bool issues = j + 2 + grp < n_tiles;
+        float tmx = -INFINITY;
+        bool mine = false;
+        if (j < n_tiles) {
+          if (j < wave_tiles) tmx = row_max(j, sc);
+          mine = vote_publish(j, tmx);
+        }
+        if (issues) issue(j + 2 + grp);
+        if (j < n_tiles) {
+          const bool sk = vote_collect(j, mine);
+          m_true = fmaxf(m_true, tmx);
+          if (j < wave_tiles && !sk) softmax(sc, tmx, pk);
+          skip_prev = sk;
+        }
+        if (!issues) wait_vmem<0>();
+        else if (j < wave_tiles) wait_copies_voted();  // a bitmap store was made
+        else wait_all_but_newest();
+        block_barrier();
+      };
+      general(0);
+      // steady iterations: every step present, no mask (as in the dense loop)
+      const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
+      int j = 1;
+      for (; j < j_ss; ++j) {
+        if (!skip_prev) pv(j - 1, pk);
+        qk(j, sc);
+        block_barrier();
+        const float tmx = tile_max(sc);
+        const bool mine = vote_publish(j, tmx);
+        issue(j + 2 + grp);
         const bool sk = vote_collect(j, mine);
         m_true = fmaxf(m_true, tmx);
-        if (j < wave_tiles && !sk) softmax(sc, tmx, pk);
+        if (!sk) softmax(sc, tmx, pk);
         skip_prev = sk;
+        wait_copies_voted();
+        block_barrier();
       }
-      if (!issues) wait_vmem<0>();
-      else if (j < wave_tiles) wait_copies_voted();  // a bitmap store was made
-      else wait_all_but_newest();
-      block_barrier();
-    };
-    general(0);
-    // steady iterations: every step present, no mask (as in the dense loop)
-    const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
-    int j = 1;
-    for (; j < j_ss; ++j) {
-      if (!skip_prev) pv(j - 1, pk);
-      qk(j, sc);
-      block_barrier();
-      const float tmx = tile_max(sc);
-      const bool mine = vote_publish(j, tmx);
-      issue(j + 2 + grp);
-      const bool sk = vote_collect(j, mine);
-      m_true = fmaxf(m_true, tmx);
-      if (!sk) softmax(sc, tmx, pk);
-      skip_prev = sk;
-      wait_copies_voted();
-      block_barrier();
+      for (; j < n_tiles; ++j) general(j);
+      finish(n_tiles - 1 < wave_tiles && !skip_prev, pk);
     }
-    for (; j <= n_tiles; ++j) general(j);
-    if (grp == 0) block_barrier();
-  }
 
-  if (SKIP && lane == 0 && skipped && p.skip_count)
-    atomicAdd(p.skip_count, (unsigned long long)skipped);
-
-  // ---- epilogue: O = acc / l (bf16, RNE), LSE = ln(sum) = (m + log2 l) ln 2
-  if (!has_rows) return;
-  const float lt = half_swap_add(l);
-  const float inv = 1.f / lt;
-  // The accumulator gives each lane 8-byte pieces of one row, so direct
-  // stores would write 16 bytes per row per instruction.  The wave's 32 x D
-  // tile goes through a private slice of the ring instead (every wave is past
-  // its last ring read here: a wave of group 0 reaches this point after the
-  // barrier that follows group 1's last P.V) and leaves as whole rows, 16
-  // bytes per lane.  The 16-byte chunk c of row r sits at chunk c ^ (r % CPR)
-  // of the slice row, which spreads a column of chunks over the banks.
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;     // rows per wave-wide store
-  static_assert(kWaves * 32 * D * 2 <= T::NST * T::STAGE, "output slices must fit in the ring");
-  LDS_AS unsigned char* ost = smem + wave * (32 * D * 2);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const u32x2 w = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
-                       pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
-      const int c = (db * 4 + g4) ^ (n % CPR);
-      *reinterpret_cast<LDS_AS u32x2*>(ost + n * (D * 2) + c * 16 + hf * 8) = w;
-    }
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = i * RPI + lane / CPR, c = lane % CPR;
-    const u32x4 w = *reinterpret_cast<const LDS_AS u32x4*>(ost + r * (D * 2) + (c ^ (r % CPR)) * 16);
-    if (q0 + r < Sq) *reinterpret_cast<u32x4*>(p.o + qrow_off(q0 + r) + c * 8) = w;
+    if (!has_next()) break;
+    prefetched = true;
+    ring = (ring + n_tiles) % T::NST;
   }
-  const int row = q0 + n;
-  if (hf == 0 && row < Sq && p.lse)
-    p.lse[PAGED ? (size_t)(qstart + row) * p.Hq + head : qbase + row] = (m_used + __log2f(lt)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool SKIP, bool PAGED = false>
@@ -686,9 +793,14 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   p.skip_map = a.skip_bitmap;
   p.skip_count = a.skip_count;
   p.nT = (a.S + BN - 1) / BN;
-  const long long grid = (long long)p.n_qblk * p.n_hgrp;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int g = (int)grid;
+  const long long items = (long long)p.n_qblk * p.n_hgrp;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  p.n_items = (int)items;
+  // Several items per workgroup hide an item's start and end behind its
+  // neighbour's, as long as every compute unit still gets a workgroup (the
+  // zigzag order balances pairs, so 1, 2 or 4).
+  p.items_per_wg = a.skip ? 1 : p.n_items >= 4 * kComputeUnits ? 4 : p.n_items >= 2 * kComputeUnits ? 2 : 1;
+  const int g = (p.n_items + p.items_per_wg - 1) / p.items_per_wg;
   if (a.skip) {
     return a.D == 64 ? launch_one<64, true, true>(p, g, stream)
                      : launch_one<128, true, true>(p, g, stream);
@@ -729,6 +841,8 @@ hipError_t launch_prefill_paged(const PagedPrefillArgs& a, hipStream_t stream) {
   const long long grid = (long long)p.n_qblk * a.N * p.n_hgrp;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const int g = (int)grid;
+  p.n_items = g;
+  p.items_per_wg = 1;
   return a.D == 64 ? launch_one<64, true, false, true>(p, g, stream)
                    : launch_one<128, true, false, true>(p, g, stream);
 }
