@@ -95,6 +95,22 @@ def test_prefill_bf16_medium_all_rows(B, Hq, Hkv, S, D, causal):
     _compare(o, lse, ro, rl, TOL["bf16"], "medium")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal", [
+    (8, 64, 64, 300, 128, True),   # 1024 work items: 4 per workgroup
+    (5, 41, 41, 1100, 64, True),   # 1025 items: 4 per workgroup, the last workgroup short
+    (4, 64, 16, 500, 128, False),  # 512 items of 64 rows x 4 heads: 2 per workgroup
+    (2, 96, 32, 700, 128, True),   # groups of 3 heads (one head per slot), 576 items: 2 each
+])
+def test_prefill_bf16_several_items_per_workgroup_all_rows(B, Hq, Hkv, S, D, causal):
+    say(f"prefill bf16 several items per workgroup, every row: B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} "
+        f"causal={causal}")
+    w = prefill_inputs(B, Hq, Hkv, S, D, seed=31 + S, causal=causal)
+    o, lse = _run_prefill(w)
+    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=causal,
+                         scale=w.scale)
+    _compare(o, lse, ro, rl, TOL["bf16"], "items")
+
+
 def test_prefill_f32_variants():
     for (B, Hq, Hkv, S, D, causal) in [(1, 4, 2, 77, 128, True), (2, 2, 1, 50, 64, False)]:
         say(f"prefill f32 B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} causal={causal}")
