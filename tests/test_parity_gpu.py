@@ -97,9 +97,10 @@ def test_prefill_bf16_medium_all_rows(B, Hq, Hkv, S, D, causal):
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,causal", [
     (8, 64, 64, 300, 128, True),   # 1024 work items: 4 per workgroup
-    (5, 41, 41, 1100, 64, True),   # 1025 items: 4 per workgroup, the last workgroup short
+    (27, 19, 19, 500, 64, True),   # 1026 items over 257 workgroups: 3 or 4 each
     (4, 64, 16, 500, 128, False),  # 512 items of 64 rows x 4 heads: 2 per workgroup
-    (2, 96, 32, 700, 128, True),   # groups of 3 heads (one head per slot), 576 items: 2 each
+    (3, 96, 32, 500, 128, True),   # groups of 3 heads (one head per slot), 576 items: 2 each
+    (5, 41, 41, 1100, 64, True),   # 1025 items, odd query-block count, 3 or 4 per workgroup
 ])
 def test_prefill_bf16_several_items_per_workgroup_all_rows(B, Hq, Hkv, S, D, causal):
     say(f"prefill bf16 several items per workgroup, every row: B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} "
