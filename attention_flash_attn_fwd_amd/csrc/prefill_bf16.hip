@@ -312,15 +312,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         const uint32_t st = smem_base + ((t + ring) % T::NST) * T::STAGE;
         const int key0 = t * BN;
         // the tile's 4 pool blocks (table entries clamped into the pool)
-        const int32_t* trow = p.table + (size_t)seq * p.max_blocks;
+        // The table is read through the constant address space: the entries
+        // are uniform and read-only, so they come by scalar loads, which the
+        // copy waits (vector-memory counts) do not see.  A vector load here
+        // would make the compiler wait for it with vmcnt(0) before the use,
+        // draining every tile copy in flight.  Entries past the sequence's
+        // last block are never selected (keys past the end are clamped to
+        // the last key), so their index is clamped instead of tested.
+        const __attribute__((address_space(4))) int32_t* trow =
+            (const __attribute__((address_space(4))) int32_t*)(p.table + (size_t)seq * p.max_blocks);
         const int nbs = (S + 15) >> 4;
         int e[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int idx = t * 4 + x;
-          const int v = idx < nbs ? trow[idx] : 0;
-          e[x] = min(max(v, 0), p.num_blocks - 1);
-        }
+        for (int x = 0; x < 4; ++x)
+          e[x] = min(max(trow[min(t * 4 + x, nbs - 1)], 0), p.num_blocks - 1);
         const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k);
         const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v);
 #pragma unroll
