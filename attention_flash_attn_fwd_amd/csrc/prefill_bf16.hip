@@ -36,6 +36,9 @@
 //    both does not overlap them on this hardware).
 //  * Causal: key tiles past a wave's last row are skipped per wave; only
 //    diagonal tiles are masked.  Heavy query blocks are scheduled first.
+//  * A workgroup runs one to four work items (query blocks) back to back;
+//    each item's last phase writes its output through LDS as whole rows and
+//    copies the next item's Q and first two K/V tiles.
 #include "attn_internal.h"
 
 #include <math.h>
