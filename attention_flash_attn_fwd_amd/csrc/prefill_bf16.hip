@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
   LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   __shared__ int vote_lds[2][kWaves];  // block skip: (tile << 1) | negligible
+  __shared__ unsigned char skip_lds[kWaves][256];  // block skip: decisions, 256 tiles a row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -516,9 +517,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // the same phase, so its vote on t arrives within a few instructions;
     // vote_collect waits for it (bounded; past the bound the tile is kept).
     // The copy issue sits between the two, hiding the LDS round trip.  One
-    // wave of the pair records the decisions on its live tiles; its bitmap
-    // store is a vector-memory operation that the phase's copy wait has to
-    // count.  vote_collect is true if tile t is skipped.
+    // wave of the pair records the decisions on its live tiles, first in an
+    // LDS row of 256 tiles, written to the bitmap when the row is full and
+    // at the end (a store per tile cost 8%).  vote_collect is true if tile t
+    // is skipped.
     const bool records = SKIP && ((slot / p.gw) & 1) == 0;
     auto vote_publish = [&](int t, float tmx_t) -> bool {
       bool neg = true;
@@ -540,12 +542,26 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       }
       const bool sk = all_neg && (other >> 1) == t && (other & 1);
       if (records && t < wave_tiles) {
-        if (lane == 0 && p.skip_map)
-          p.skip_map[(((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT + t] = sk ? 1 : 0;
+        if (lane == 0) skip_lds[wave][t & 255] = sk ? 1 : 0;
         skipped += sk ? 1u : 0u;
       }
       return sk;
     };
+    // A recording wave's decisions on tiles t0 .. t0+255 from its LDS row to
+    // the bitmap, a byte per lane and store.  The buffer resource ends at the
+    // wave's last live tile, so the range check drops the rest and exactly
+    // four stores are issued, which the copy wait of the phase counts.
+    auto flush_skips = [&](int t0) {
+      uint8_t* row = p.skip_map == nullptr
+                         ? nullptr
+                         : p.skip_map + (((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row ? wave_tiles : 0, kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b8(skip_lds[wave][i * 64 + lane], rs, t0 + i * 64 + lane, 0, 0);
+    };
+    // a full row of decisions is written in the phase of its last tile
+    auto flush_due = [&](int t) { return records && t < wave_tiles && (t & 255) == 255; };
 
     // The last phase pair of the item: P.V of its last tile, then a VALU
     // phase with no tile work left, which takes the epilogue and, when the
@@ -568,8 +584,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     auto finish = [&](bool do_pv, uint32_t (*pk)[8]) {
       if (do_pv) pv(n_tiles - 1, pk);
       block_barrier();
-      if (SKIP && lane == 0 && skipped && p.skip_count)
-        atomicAdd(p.skip_count, (unsigned long long)skipped);
+      if constexpr (SKIP) {
+        if (records && wave_tiles > 0) flush_skips((wave_tiles - 1) & ~255);  // the last row
+        if (lane == 0 && skipped && p.skip_count)
+          atomicAdd(p.skip_count, (unsigned long long)skipped);
+      }
       const float lt = half_swap_add(l);
       const float inv = 1.f / lt;
       static_assert(4 * 32 * D * 2 <= T::STAGE, "four output slices must fit in a stage");
@@ -703,11 +722,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       }
       // wait for the copies before the newest, with this phase's bitmap store
       // (issued after them) left in flight as well
-      const bool stores = records && p.skip_map;
-      auto wait_copies_voted = [&]() {
-        if (!stores) wait_all_but_newest();
-        else if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 1>();
-        else wait_vmem<DMA_HI + 1>();
+      // the copy wait of a phase whose four bitmap stores follow its copies
+      auto wait_copies_flushed = [&]() {
+        if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 4>(); else wait_vmem<DMA_HI + 4>();
       };
       auto general = [&](int j) {
         if (j >= 1 && j - 1 < wave_tiles && !skip_prev) pv(j - 1, pk);
@@ -721,14 +738,16 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
           mine = vote_publish(j, tmx);
         }
         if (issues) issue(j + 2 + grp);
+        const bool flush = flush_due(j);
         if (j < n_tiles) {
           const bool sk = vote_collect(j, mine);
+          if (flush) flush_skips(j - 255);
           m_true = fmaxf(m_true, tmx);
           if (j < wave_tiles && !sk) softmax(sc, tmx, pk);
           skip_prev = sk;
         }
         if (!issues) wait_vmem<0>();
-        else if (j < wave_tiles) wait_copies_voted();  // a bitmap store was made
+        else if (flush) wait_copies_flushed();
         else wait_all_but_newest();
         block_barrier();
       };
@@ -744,10 +763,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         const bool mine = vote_publish(j, tmx);
         issue(j + 2 + grp);
         const bool sk = vote_collect(j, mine);
+        const bool flush = flush_due(j);
+        if (flush) flush_skips(j - 255);
         m_true = fmaxf(m_true, tmx);
         if (!sk) softmax(sc, tmx, pk);
         skip_prev = sk;
-        wait_copies_voted();
+        if (flush) wait_copies_flushed(); else wait_all_but_newest();
         block_barrier();
       }
       for (; j < n_tiles; ++j) general(j);
