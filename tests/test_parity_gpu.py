@@ -101,6 +101,8 @@ def test_prefill_bf16_medium_all_rows(B, Hq, Hkv, S, D, causal):
     (4, 64, 16, 500, 128, False),  # 512 items of 64 rows x 4 heads: 2 per workgroup
     (3, 96, 32, 500, 128, True),   # groups of 3 heads (one head per slot), 576 items: 2 each
     (5, 41, 41, 1100, 64, True),   # 1025 items, odd query-block count, 3 or 4 per workgroup
+    (16, 64, 64, 50, 128, True),   # 1024 one-tile items: the ring moves one stage an item
+    (16, 64, 64, 100, 64, False),  # 1024 two-tile items, non-causal
 ])
 def test_prefill_bf16_several_items_per_workgroup_all_rows(B, Hq, Hkv, S, D, causal):
     say(f"prefill bf16 several items per workgroup, every row: B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} "
