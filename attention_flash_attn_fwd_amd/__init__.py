@@ -116,9 +116,22 @@ def _check(st: int, where: str) -> None:
 
 
 def _dev(*ts):
+    """All given tensors on one GPU, the current one: the library launches on
+    the current device's stream and checks that device's architecture."""
+    idx = None
     for t in ts:
-        if t is not None and t.device.type != "cuda":
+        if t is None:
+            continue
+        if t.device.type != "cuda":
             raise ValueError("tensors must live on the GPU")
+        i = t.device.index if t.device.index is not None else torch.cuda.current_device()
+        if idx is None:
+            idx = i
+        elif i != idx:
+            raise ValueError("tensors must live on one GPU")
+    if idx is not None and idx != torch.cuda.current_device():
+        raise ValueError(f"tensors live on cuda:{idx} but the current device is "
+                         f"cuda:{torch.cuda.current_device()}; call under torch.cuda.device({idx})")
 
 
 # ---------------------------------------------------- C-ABI mirrors (in-place)
