@@ -286,6 +286,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       drow[j] = g / sl;
       doff[j] = (uint32_t)drow[j] * T::RB + (c < T::CH ? c : 0) * 16;
     }
+    // Paged, whole tiles: the lane's row r of slot j lies in pool block r / 16
+    // of the tile's four, at the same offset in every tile, so pool + that
+    // offset is fixed per item and a copy adds the block's base (entry x
+    // block bytes).  A slot's rows touch at most two adjacent pool blocks.
+    const unsigned char* pvrow[DMA_HI];
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int j = 0; j < DMA_HI; ++j) {
+        const int i = wave + j * kWaves;
+        const int r = drow[j];
+        pvrow[j] = reinterpret_cast<const unsigned char*>(i < T::KSL ? p.k : p.v) +
+                   (((size_t)kvh << 4) + (r & 15)) * T::RB + (doff[j] - (uint32_t)r * T::RB);
+      }
+    }
     // Dense tile t of the item whose K and V start at kg and vg, into stage
     // (t + rg) % NST.
     auto issue_dense = [&](const uint16_t* kg, const uint16_t* vg, int t, int rg) {
@@ -327,9 +341,30 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
             (const __attribute__((address_space(4))) int32_t*)(p.table + (size_t)seq * p.max_blocks);
         const int nbs = (S + 15) >> 4;
         int e[4];
+        if (t * 4 + 3 < nbs) {  // four adjacent entries: one scalar load
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          e[x] = min(max(trow[min(t * 4 + x, nbs - 1)], 0), p.num_blocks - 1);
+          for (int x = 0; x < 4; ++x) e[x] = trow[t * 4 + x];
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) e[x] = trow[min(t * 4 + x, nbs - 1)];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) e[x] = min(max(e[x], 0), p.num_blocks - 1);
+        if (key0 + BN <= S) {
+          const uint32_t bs = (uint32_t)p.Hkv * 16 * T::RB;  // bytes of one pool block
+#pragma unroll
+          for (int j = 0; j < DMA_HI; ++j) {
+            const int i = wave + j * kWaves;
+            if (j == DMA_LO && !dma_hi) break;
+            // the slot's first pool block (uniform) and, per lane, it or the next
+            const int x0 = __builtin_amdgcn_readfirstlane(drow[j]) >> 4;
+            const int ea = x0 == 0 ? e[0] : x0 == 1 ? e[1] : x0 == 2 ? e[2] : e[3];
+            const int eb = x0 == 0 ? e[1] : x0 == 1 ? e[2] : e[3];
+            const uint32_t ph = (uint32_t)((drow[j] >> 4) == x0 ? ea : eb);
+            dma16_va(pvrow[j] + (size_t)ph * bs, st + i * 1024);
+          }
+          return;
+        }
         const unsigned char* kpool = reinterpret_cast<const unsigned char*>(p.k);
         const unsigned char* vpool = reinterpret_cast<const unsigned char*>(p.v);
 #pragma unroll

@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -167,7 +168,17 @@ def main():
     }
 
     def time_it(fn, reps, warm=2):
-        """Mean time per launch of `reps` back-to-back launches (HIP events)."""
+        """Mean time per launch of `reps` back-to-back launches (HIP events).
+        Short launches get more of both: at least about 30 ms of warm-up
+        launches (the clock takes some ms of load to settle) and about 10 ms
+        of timed ones."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        t1 = max(time.perf_counter() - t0, 1e-6)
+        warm = max(warm, min(1000, math.ceil(0.03 / t1)))
+        reps = max(reps, min(1000, math.ceil(0.01 / t1)))
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
