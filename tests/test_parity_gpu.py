@@ -263,8 +263,9 @@ def _run_prefill_paged(d):
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 128), (16, 2, 64), (8, 1, 128)])
 def test_prefill_paged_varlen(Hq, Hkv, D):
-    ctx = [0, 37, 1000, 5, 300, 0, 64]
-    ql = [200, 1, 300, 600, 63, 1, 257]
+    # the last two have 512 and 128 keys: every tile whole, the last included
+    ctx = [0, 37, 1000, 5, 300, 0, 64, 448, 0]
+    ql = [200, 1, 300, 600, 63, 1, 257, 64, 128]
     say(f"chunked paged prefill Hq{Hq} Hkv{Hkv} D{D} ctx={ctx} q={ql}")
     d = paged_prefill_inputs(ctx, ql, Hq, Hkv, D, seed=120 + D + Hq, tail="nan")
     o, lse = _run_prefill_paged(d)
