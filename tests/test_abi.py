@@ -184,3 +184,23 @@ def test_decode_fp8_validation_without_device():
     assert call(Hq=64, Hkv=2) == -2
     assert call(ws=None) == -4
     assert call(wsb=need - 1) == -4
+
+
+def test_binding_device_check(monkeypatch):
+    """The binding takes tensors of one GPU, the current one (stand-ins here:
+    only the device attribute is read, and the current device is patched)."""
+    import types
+    import torch
+
+    def t(dev):
+        return types.SimpleNamespace(device=torch.device(dev))
+
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 1)
+    A._dev(t("cuda:1"), None, t("cuda:1"))          # same GPU as the current one
+    with pytest.raises(ValueError, match="current device"):
+        A._dev(t("cuda:0"), t("cuda:0"))
+    with pytest.raises(ValueError, match="one GPU"):
+        A._dev(t("cuda:1"), t("cuda:0"))
+    with pytest.raises(ValueError, match="on the GPU"):
+        A._dev(t("cuda:1"), t("cpu"))
+    A._dev(None, None)                              # nothing to check
