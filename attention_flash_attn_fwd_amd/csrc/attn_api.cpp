@@ -231,6 +231,7 @@ int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int total_q, 
   if (block_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if ((long long)max_blocks_per_seq * 16 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (Hkv > 65535) return ATTN_ERR_UNSUPPORTED;  // pool block bytes stay 32-bit
   int st = check_device();
   if (st != ATTN_OK) return st;
   attn::PagedPrefillArgs a{q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse,

@@ -253,6 +253,7 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
  *   k_pool/v_pool : bf16, kv_layout must be ATTN_KV_ROWMAJOR
  *                   ([num_blocks, Hkv, 16, D]; ATTN_ERR_UNSUPPORTED otherwise)
  *   block_table   : int32 [num_seqs, max_blocks_per_seq]
+ * Hkv above 65535 gives ATTN_ERR_UNSUPPORTED, as in the decode.
  * Requirements on the device data (not checked on the host): Sq <= Sk and
  * Sk <= 16 * max_blocks_per_seq (a sequence breaking them gets NaN rows),
  * Sq <= max_seqlen_q, valid table entries (out-of-range entries are

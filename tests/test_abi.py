@@ -159,6 +159,7 @@ def test_prefill_paged_validation_without_device():
     assert call(lay=1) == -2           # MFMA-native pools: not supported here
     assert call(bs=32) == -2
     assert call(D=96) == -2
+    assert call(Hq=70000, Hkv=70000) == -2   # pool block bytes must stay 32-bit
 
 
 def test_decode_fp8_validation_without_device():
