@@ -102,11 +102,14 @@ def ref_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
             kg, vg = k[b, g], v[b, g]
             for r0 in range(0, R, row_block):
                 ri = rows[r0:r0 + row_block]
-                s = scale * (q[b, h, ri, :] @ kg.T)            # [rb, S]
+                # causal: keys past the block's last row are masked for every
+                # row of the block, so their scores are not formed
+                nk = int(ri.max()) + 1 if causal else S
+                s = scale * (q[b, h, ri, :] @ kg[:nk].T)        # [rb, nk]
                 if causal:
-                    s = np.where(np.arange(S)[None, :] <= ri[:, None], s, -np.inf)
+                    s = np.where(np.arange(nk)[None, :] <= ri[:, None], s, -np.inf)
                 p, l = _softmax_rows(s)
-                out[b, h, r0:r0 + row_block] = p @ vg
+                out[b, h, r0:r0 + row_block] = p @ vg[:nk]
                 lse[b, h, r0:r0 + row_block] = l
     return out, lse
 
@@ -181,7 +184,9 @@ def ref_blockskip(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     are left out.  Because a skipped tile has tm_r < m_r for every row (ln lam
     < 0), folding it into the maximum changes nothing, so the running max
     before tile kt equals the plain prefix maximum over ALL tiles kt' < kt;
-    that is what is evaluated here.
+    that is what is evaluated here (a cumulative maximum over the tile row
+    maxima, shifted by one tile).  Keys of tiles past qt are masked for every
+    row of query tile qt, so their scores are not formed.
 
     Returns (O [B,Hq,R,D], LSE [B,Hq,R], skip [B,Hq,nQ,nK] bool,
     gap [B,Hq,nQ,nK] float64) for the chosen query tiles (default: all),
@@ -209,29 +214,29 @@ def ref_blockskip(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
             r_out = 0
             for i, qt in enumerate(qtiles):
                 ri = row_list[i]
-                s = scale * (q[b, h, ri, :] @ kg.T)                     # [T, S]
-                vis = np.arange(S)[None, :] <= ri[:, None]
+                nt = int(qt) + 1                       # key tiles 0..qt
+                nk = min(S, nt * tile)                 # their keys
+                s = scale * (q[b, h, ri, :] @ kg[:nk].T)                # [R, nk]
+                vis = np.arange(nk)[None, :] <= ri[:, None]
                 s = np.where(vis, s, -np.inf)
-                # tile row maxima tm[r, kt], kt = 0..nT-1
-                tm = np.full((len(ri), nT), -np.inf)
-                for kt in range(int(qt) + 1):
-                    tm[:, kt] = np.max(s[:, kt * tile:(kt + 1) * tile], axis=1)
-                for kt in range(int(qt) + 1):
-                    if kt == 0:
-                        m_prev = np.full(len(ri), -np.inf)
-                    else:
-                        m_prev = np.max(tm[:, :kt], axis=1)
-                    with np.errstate(invalid="ignore"):
-                        d = tm[:, kt] - m_prev
-                    neg = np.isneginf(tm[:, kt]) | (np.isfinite(m_prev) & (d < ln_lam))
-                    skip[b, h, i, kt] = bool(np.all(neg))
-                    gap[b, h, i, kt] = np.inf if kt == 0 else float(np.max(d))
-                keep = np.ones_like(vis)
-                for kt in np.nonzero(skip[b, h, i])[0]:
-                    keep[:, kt * tile:(kt + 1) * tile] = False
-                s = np.where(keep, s, -np.inf)
+                # tile row maxima tm[r, kt], kt = 0..qt (a partial last tile
+                # is padded with -inf, which leaves its maxima unchanged)
+                padded = np.full((len(ri), nt * tile), -np.inf)
+                padded[:, :nk] = s
+                tm = padded.reshape(len(ri), nt, tile).max(axis=2)      # [R, nt]
+                # running maximum before tile kt: maximum over tiles 0..kt-1
+                m_prev = np.concatenate([np.full((len(ri), 1), -np.inf),
+                                         np.maximum.accumulate(tm, axis=1)[:, :-1]], axis=1)
+                with np.errstate(invalid="ignore"):
+                    d = tm - m_prev
+                neg = np.isneginf(tm) | (np.isfinite(m_prev) & (d < ln_lam))
+                skip[b, h, i, :nt] = np.all(neg, axis=0)
+                gap[b, h, i, :nt] = np.max(d, axis=0)
+                gap[b, h, i, 0] = np.inf
+                keep = ~np.repeat(skip[b, h, i, :nt], tile)[:nk]
+                s = np.where(keep[None, :], s, -np.inf)
                 p, l = _softmax_rows(s)
-                out[b, h, r_out:r_out + len(ri)] = p @ vg
+                out[b, h, r_out:r_out + len(ri)] = p @ vg[:nk]
                 lse[b, h, r_out:r_out + len(ri)] = l
                 r_out += len(ri)
     return out, lse, skip, gap

@@ -625,3 +625,27 @@ def test_fp8_decode_within_quantisation_bound():
             assert abs(l[n, h] - l_ref[n, h]) <= E + 1e-12
     # and the bound is not vacuous: the quantised result is close
     assert np.abs(o - o_ref).max() < 0.25
+
+
+def test_oracle_pool_equals_direct_calls():
+    """The worker pool the full-size GPU tests use returns exactly what the
+    oracle returns when called directly (float32 inputs widened exactly)."""
+    from _oracle_pool import oracle_map
+    from workloads import blockskip_inputs
+    w = blockskip_inputs(1, 4, 2, 200, 16, seed=64, amplitude=12.0, n_sinks=3,
+                         boosted="second_half", scale=0.3)
+    q, k, v = w.q.float().numpy(), w.k.float().numpy(), w.v.float().numpy()
+    jobs = [((q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1]),
+             dict(scale=w.scale, lam=1e-3, tile=64)) for h in range(4)]
+    res = oracle_map("ref_blockskip", jobs)
+    full = ref_blockskip(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), scale=w.scale,
+                         lam=1e-3, tile=64)
+    for h in range(4):
+        for i in range(4):
+            np.testing.assert_array_equal(res[h][i][0, 0], full[i][0, h])
+    res = oracle_map("ref_prefill", [(a, dict(scale=w.scale, causal=True)) for a, _ in jobs])
+    o, l = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=True,
+                       scale=w.scale)
+    for h in range(4):
+        np.testing.assert_array_equal(res[h][0][0, 0], o[0, h])
+        np.testing.assert_array_equal(res[h][1][0, 0], l[0, h])

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import attention_flash_attn_fwd_amd as A
+from _oracle_pool import oracle_map
 from oracle import (ref_blockskip, ref_decode_paged, ref_decode_paged_blockskip, ref_prefill,
                     ref_prefill_paged)
 from workloads import (CONFIGS, blockskip_inputs, decode_inputs, paged_prefill_inputs,
@@ -124,35 +125,39 @@ def test_prefill_f32_variants():
         _compare(o, lse, ro, rl, TOL["f32"], "f32")
 
 
-def _sampled_rows(S, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(S, size=n, replace=False).tolist())
-    rows |= {0, 1, 63, 64, S // 2, S - 2, S - 1}
-    return np.array(sorted(rows))
+def _head_jobs(w, **kw):
+    """One oracle job per (batch, query head): that head's Q and its group's
+    K/V, as float32 (exact for bf16; widened to float64 in the worker)."""
+    q, k, v = w.q.float().numpy(), w.k.float().numpy(), w.v.float().numpy()
+    G = w.Hq // w.Hkv
+    return [((q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1], v[b:b + 1, h // G:h // G + 1]),
+             dict(scale=w.scale, **kw)) for b in range(w.B) for h in range(w.Hq)]
+
+
+def _oracle_prefill_all(w, causal):
+    """ref_prefill over every (batch, head) and every row, in worker processes."""
+    res = oracle_map("ref_prefill", _head_jobs(w, causal=causal))
+    ro = np.stack([r[0][0, 0] for r in res]).reshape(w.B, w.Hq, w.S, w.D)
+    rl = np.stack([r[1][0, 0] for r in res]).reshape(w.B, w.Hq, w.S)
+    return ro, rl
 
 
 @pytest.mark.parametrize("name", ["mha_causal_s2048", "gqa_causal_s8192"])
-def test_prefill_full_size_sampled_rows(name):
+def test_prefill_full_size_every_row(name):
     c = CONFIGS[name]
-    say(f"{name} full size, sampled rows")
+    say(f"{name} full size (the launch the bench times), every row of every head")
     w = prefill_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"])
     o, lse = _run_prefill(w)
-    rows = _sampled_rows(c["S"], 48, 7)
-    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=True,
-                         scale=w.scale, rows=rows)
-    _compare(o[:, :, rows], lse[:, :, rows], ro, rl, TOL["bf16"], name)
-    # property at every row: |O| is bounded by max |V| of the visible prefix
-    assert np.abs(o).max() <= float(w.v.float().abs().max()) + 1e-2
+    ro, rl = _oracle_prefill_all(w, True)
+    _compare(o, lse, ro, rl, TOL["bf16"], name)
 
 
-def test_prefill_noncausal_gqa_s8192_sampled_rows():
-    say("non-causal GQA B1 Hq32 Hkv8 S8192 D128, sampled rows")
+def test_prefill_noncausal_gqa_s8192_every_row():
+    say("non-causal GQA B1 Hq32 Hkv8 S8192 D128, every row of every head")
     w = prefill_inputs(1, 32, 8, 8192, 128, seed=1013, causal=False)
     o, lse = _run_prefill(w)
-    rows = _sampled_rows(8192, 32, 9)
-    ro, rl = ref_prefill(upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v), causal=False,
-                         scale=w.scale, rows=rows)
-    _compare(o[:, :, rows], lse[:, :, rows], ro, rl, TOL["bf16"], "noncausal s8192")
+    ro, rl = _oracle_prefill_all(w, False)
+    _compare(o, lse, ro, rl, TOL["bf16"], "noncausal s8192")
 
 
 # -------------------------------------------------------------------- decode
@@ -370,13 +375,14 @@ def _run_blockskip(w, lam):
     return o.float().cpu().numpy(), lse.cpu().numpy(), bm.cpu().numpy(), int(cnt.item())
 
 
-def _check_decisions(bm, skip, gap, lam, qtiles, what):
+def _check_decisions(bm, skip, gap, lam, what):
+    """Every live tile's decision (kt <= qt) equals the oracle's, except tiles
+    whose margin |gap - ln(lambda)| is below 1e-3 (fp64 oracle against fp32
+    kernel), which are counted."""
     ln_lam = math.log(lam)
     nT = bm.shape[-1]
-    live = np.zeros_like(skip)
-    for i, qt in enumerate(qtiles):
-        live[:, :, i, : qt + 1] = True
-    gpu = bm[:, :, qtiles, :].astype(bool) & live
+    live = np.broadcast_to(np.tril(np.ones((nT, nT), dtype=bool)), skip.shape)
+    gpu = bm.astype(bool) & live
     border = live & (np.abs(gap - ln_lam) < 1e-3)
     mism = (gpu != skip) & live & ~border
     say(f"{what}: skipped {int(skip.sum())}/{int(live.sum())} live tiles, "
@@ -385,18 +391,44 @@ def _check_decisions(bm, skip, gap, lam, qtiles, what):
     return int(border.sum())
 
 
-def test_blockskip_stress_full_decisions():
-    say("block skip stress: S=4096 amplitude 12, second half boosted")
-    w = blockskip_inputs(1, 8, 2, 4096, 128, seed=1105, amplitude=12.0, boosted="second_half")
-    o, lse, bm, cnt = _run_blockskip(w, 1e-3)
-    q, k, v = upcast_f64(w.q), upcast_f64(w.k), upcast_f64(w.v)
-    ro, rl, skip, gap = ref_blockskip(q, k, v, scale=w.scale, lam=1e-3, tile=64)
-    nT = 4096 // 64
-    _check_decisions(bm, skip, gap, 1e-3, np.arange(nT), "stress")
-    live = 8 * nT * (nT + 1) // 2
-    assert skip.sum() > 0.1 * live, "stress inputs must exercise the skip path"
+def _oracle_blockskip_all(w, lam):
+    """ref_blockskip over every (batch, head) and every query tile, in worker
+    processes."""
+    res = oracle_map("ref_blockskip", _head_jobs(w, lam=lam, tile=64))
+    nT = (w.S + 63) // 64
+    ro = np.stack([r[0][0, 0] for r in res]).reshape(w.B, w.Hq, w.S, w.D)
+    rl = np.stack([r[1][0, 0] for r in res]).reshape(w.B, w.Hq, w.S)
+    skip = np.stack([r[2][0, 0] for r in res]).reshape(w.B, w.Hq, nT, nT)
+    gap = np.stack([r[3][0, 0] for r in res]).reshape(w.B, w.Hq, nT, nT)
+    return ro, rl, skip, gap
+
+
+def _check_blockskip_all(w, lam, what, min_frac=0.0):
+    o, lse, bm, cnt = _run_blockskip(w, lam)
+    ro, rl, skip, gap = _oracle_blockskip_all(w, lam)
+    _check_decisions(bm, skip, gap, lam, what)
+    nT = (w.S + 63) // 64
+    live = w.B * w.Hq * nT * (nT + 1) // 2
     assert cnt == int(bm.astype(np.int64).sum())
-    _compare(o, lse, ro, rl, TOL["bf16"], "stress O/LSE")
+    assert skip.sum() >= min_frac * live, "the input must exercise the skip path"
+    _compare(o, lse, ro, rl, TOL["bf16"], f"{what} O/LSE")
+    say(f"{what}: skipped fraction {cnt / live:.6f} ({cnt}/{live})")
+    return cnt, live
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D", [
+    (1, 8, 2, 4096, 128),    # groups of 4 heads (the block-skip workload's grouping)
+    (1, 8, 8, 2048, 128),    # MHA: one head per workgroup, pairs of adjacent waves
+    (1, 6, 3, 2048, 128),    # groups of 2 heads
+    (1, 8, 4, 1500, 64),     # D = 64, ragged last tile
+    (1, 16, 2, 2048, 128),   # groups of 8 heads, split over two workgroups
+    (2, 4, 2, 2048, 128),    # two batches: bitmap rows of batch 1
+])
+def test_blockskip_stress_full_decisions(B, Hq, Hkv, S, D):
+    say(f"block skip stress: B{B} Hq{Hq} Hkv{Hkv} S{S} D{D} amplitude 12, second half boosted")
+    w = blockskip_inputs(B, Hq, Hkv, S, D, seed=1105 + S + Hq, amplitude=12.0,
+                         boosted="second_half")
+    _check_blockskip_all(w, 1e-3, f"stress B{B} Hq{Hq} Hkv{Hkv} S{S} D{D}", min_frac=0.02)
 
 
 def test_blockskip_small_lambda_equals_dense():
@@ -408,27 +440,21 @@ def test_blockskip_small_lambda_equals_dense():
     assert np.array_equal(o, od) and np.array_equal(lse, ld)
 
 
-def test_blockskip_full_config_sampled_qtiles():
+def test_blockskip_full_config_every_tile():
     c = CONFIGS["blockskip_s32768"]
-    say("blockskip_s32768 full size, sampled query tiles")
+    say("blockskip_s32768 full size: every decision, O and LSE of every head")
     w = blockskip_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"],
                          amplitude=c["amplitude"], boosted=c["boosted"])
-    o, lse, bm, cnt = _run_blockskip(w, c["lam"])
-    qt = np.array([0, 1, 7, 100, 256, 511])
-    heads = [0, 13, 31]
-    res = []
-    for h in heads:
-        g = h // (c["Hq"] // c["Hkv"])
-        res.append(ref_blockskip(upcast_f64(w.q[:, h:h + 1]), upcast_f64(w.k[:, g:g + 1]),
-                                 upcast_f64(w.v[:, g:g + 1]), scale=w.scale, lam=c["lam"],
-                                 tile=64, qtiles=qt))
-    ro, rl, skip, gap = (np.concatenate([r[i] for r in res], axis=1) for i in range(4))
-    _check_decisions(bm[:, heads], skip, gap, c["lam"], qt, "c5 sampled")
-    rows = np.concatenate([np.arange(t * 64, (t + 1) * 64) for t in qt])
-    _compare(o[:, heads][:, :, rows], lse[:, heads][:, :, rows], ro, rl, TOL["bf16"], "c5 O/LSE")
-    nT = c["S"] // 64
-    live = c["B"] * c["Hq"] * nT * (nT + 1) // 2
-    say(f"c5 skipped fraction {cnt / live:.6f} ({cnt}/{live})")
+    _check_blockskip_all(w, c["lam"], "blockskip_s32768")
+
+
+def test_blockskip_full_size_stress_every_tile():
+    c = CONFIGS["blockskip_s32768"]
+    say("block skip stress at S=32768 (amplitude 12, second half boosted): every decision, "
+        "O and LSE of every head")
+    w = blockskip_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"],
+                         amplitude=12.0, boosted="second_half")
+    _check_blockskip_all(w, c["lam"], "blockskip_s32768 stress", min_frac=0.3)
 
 
 # ------------------------------------------------------------ FP8 KV decode
