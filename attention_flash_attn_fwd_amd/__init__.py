@@ -7,7 +7,7 @@ call fails, an exception is raised.
 
 The functions named like the C entry points (``attn_prefill``,
 ``attn_prefill_f32``, ``attn_prefill_blockskip``, ``attn_decode_paged``,
-``attn_decode_workspace_bytes``, ``attn_status_string``) take caller-allocated
+``attn_decode_workspace_bytes``, ``attn_status_string``, ...) take caller-allocated
 torch tensors; ``prefill``, ``prefill_blockskip`` and ``decode_paged``
 allocate the outputs and return them.
 """
@@ -23,10 +23,14 @@ __all__ = [
     "AttnError", "lib_path", "load", "attn_status_string", "attn_arch_supported",
     "attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
     "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_paged_blockskip",
-    "attn_prefill_paged", "attn_decode_paged_fp8",
+    "attn_prefill_paged", "attn_decode_paged_fp8", "attn_decode_paged_noalloc",
+    "DECODE_STATIC_SCRATCH_BYTES",
     "prefill", "prefill_blockskip", "decode_paged", "decode_paged_blockskip", "prefill_paged",
-    "decode_paged_fp8",
+    "decode_paged_fp8", "decode_paged_noalloc",
 ]
+
+# ATTN_DECODE_STATIC_SCRATCH_BYTES of include/attn.h
+DECODE_STATIC_SCRATCH_BYTES = 16 << 20
 
 _LIB: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
@@ -73,6 +77,9 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_paged.restype = _I
     lib.attn_prefill_paged.argtypes = [_P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I,
                                        _I, _I, _I, _F, _P]
+    lib.attn_decode_paged_noalloc.restype = _I
+    lib.attn_decode_paged_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I,
+                                              _I, _I, _F, _P]
     lib.attn_decode_paged_blockskip.restype = _I
     lib.attn_decode_paged_blockskip.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I,
                                                 _I, _I, _I, _F, _F, _P, _P, _P, ctypes.c_size_t,
@@ -242,6 +249,32 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int,
     _check(st, "attn_decode_paged")
 
 
+def attn_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o, lse,
+                              scale: float, stream=None, layout: str = "rowmajor") -> None:
+    """Paged decode into caller-allocated o and lse (or None) with the
+    library's static scratch in place of a workspace (no device allocation
+    in the call; requests larger than DECODE_STATIC_SCRATCH_BYTES raise)."""
+    N, Hq, D = q.shape
+    NB, Hkv = k_pool.shape[0], k_pool.shape[1]
+    _dev(q, k_pool, v_pool, block_table, seq_lens, o, lse)
+    if layout not in KV_LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}")
+    ks, vs = _pool_shapes(NB, Hkv, block_size, D, layout)
+    if tuple(k_pool.shape) != ks or tuple(v_pool.shape) != vs or o.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != N or seq_lens.shape != (N,):
+        raise ValueError("block_table must be [N, max_blocks], seq_lens [N]")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq)):
+        raise ValueError("lse must be float32 [N,Hq]")
+    st = load().attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), int(block_size),
+        KV_LAYOUTS[layout], _ptr(o), _ptr(lse), N, Hq, Hkv, D, NB, int(block_table.shape[1]),
+        float(scale), _stream(stream))
+    _check(st, "attn_decode_paged_noalloc")
+
+
 def attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o,
                                 lse, scale: float, lam: float, workspace, skip_bitmap=None,
                                 skipped_blocks=None, stream=None, layout: str = "mfma") -> None:
@@ -366,6 +399,20 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size: int = 16,
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse, scale,
                       workspace, layout=layout)
+    return o, lse
+
+
+def decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, block_size: int = 16,
+                         scale: Optional[float] = None, layout: str = "rowmajor"):
+    """Allocate O and LSE and run the paged decode on the library's static
+    scratch (the call itself allocates no workspace)."""
+    N, Hq, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    attn_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse, scale,
+                              layout=layout)
     return o, lse
 
 

@@ -21,7 +21,7 @@ bool arch_name_ok(const char* name) {
   return strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
 }
 
-int check_device() {
+int check_device(int* device = nullptr) {
   int dev = -1;
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return ATTN_ERR_NO_DEVICE;
@@ -34,6 +34,7 @@ int check_device() {
     st = arch_name_ok(prop.gcnArchName) ? 1 : -1;
     g_arch_state[dev].store(st, std::memory_order_relaxed);
   }
+  if (device) *device = dev;
   return st == 1 ? ATTN_OK : ATTN_ERR_ARCH;
 }
 
@@ -68,6 +69,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP runtime or launch error";
     case ATTN_ERR_NO_DEVICE: return "no HIP device visible";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "request needs more than the static decode scratch (ATTN_DECODE_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -124,7 +127,7 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool,
                   int num_blocks, int max_blocks_per_seq, float scale, void* workspace,
                   size_t workspace_bytes, int skip, float lambda, uint8_t* skip_bitmap,
                   unsigned long long* skipped_blocks, int fp8, float k_scale, float v_scale,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool static_scratch = false) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
   if (num_seqs < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
     return ATTN_ERR_INVALID_ARG;
@@ -142,10 +145,19 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool,
   if ((long long)ns > 65535 || (long long)Hkv > 65535 || (long long)num_seqs > 65535)
     return ATTN_ERR_UNSUPPORTED;
   const size_t need = attn_decode_workspace_bytes(num_seqs, Hq, D, max_blocks_per_seq, block_size);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 15u) != 0) return ATTN_ERR_WORKSPACE;
-  int st = check_device();
+  if (static_scratch) {
+    if (need > ATTN_DECODE_STATIC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH_LIMIT;
+  } else {
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 15u) != 0) return ATTN_ERR_WORKSPACE;
+  }
+  int dev = -1;
+  int st = check_device(&dev);
   if (st != ATTN_OK) return st;
+  if (static_scratch) {
+    // the array's device address on the current GPU, never its host name
+    if (attn::decode_static_scratch(dev, &workspace) != hipSuccess) return ATTN_ERR_HIP;
+  }
   attn::DecodeArgs a;
   a.q = q;
   a.k_pool = k_pool;
@@ -188,6 +200,16 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, kv_layout, o, lse,
                        num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, workspace,
                        workspace_bytes, 0, 0.f, nullptr, nullptr, 0, 1.f, 1.f, stream);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int block_size, int kv_layout, void* o, float* lse, int num_seqs,
+                              int Hq, int Hkv, int D, int num_blocks, int max_blocks_per_seq,
+                              float scale, hipStream_t stream) {
+  return decode_common(q, k_pool, v_pool, block_table, seq_lens, block_size, kv_layout, o, lse,
+                       num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, scale, nullptr, 0, 0,
+                       0.f, nullptr, nullptr, 0, 1.f, 1.f, stream, /*static_scratch=*/true);
 }
 
 int attn_decode_paged_blockskip(const void* q, const void* k_pool, const void* v_pool,

@@ -79,4 +79,10 @@ inline int decode_num_splits(int max_blocks, int block_size) {
 
 hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream);
 
+// Device address of the library's static decode scratch
+// (ATTN_DECODE_STATIC_SCRATCH_BYTES) on `device`, which must be the current
+// device.  Resolved with hipGetSymbolAddress on the first call per device and
+// kept; later calls make no HIP call.
+hipError_t decode_static_scratch(int device, void** addr);
+
 }  // namespace attn

@@ -30,7 +30,40 @@
 
 #include <math.h>
 
+#include <atomic>
+
+#include "../../include/attn.h"
+
+// Split-KV scratch of the allocation-free decode entry point: the partial
+// outputs and log-sum-exps of one call, for callers that cannot allocate
+// device memory.  Each GPU the library runs on holds one copy until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol): decode_static_scratch resolves the
+// device address per GPU.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_STATIC_SCRATCH_BYTES];
+
 namespace attn {
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+}  // namespace
+
+hipError_t decode_static_scratch(int device, void** addr) {
+  if (device < 0 || device >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[device].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // the caller made `device` current; every GPU has its own copy of the
+    // array at its own address (racing first calls store the same value)
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[device].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -5,7 +5,9 @@
  * given HIP stream and returns an attn_status code; it never synchronises the
  * device.  All tensor pointers are DEVICE pointers owned by the caller; the
  * library allocates no device memory and keeps no state between calls apart
- * from a one-time check of the device architecture.  Arguments are validated
+ * from a one-time check of the device architecture and, for
+ * attn_decode_paged_noalloc, a static scratch array per GPU (part of the
+ * library's code object) and its device address.  Arguments are validated
  * on the host before any HIP call; a call that returns an error has enqueued
  * nothing.  Values inside device buffers (sequence lengths, block-table
  * entries) cannot be checked on the host: see attn_decode_paged for how the
@@ -57,8 +59,15 @@ typedef enum {
   ATTN_ERR_ARCH = -3,        /* current device is not gfx950                         */
   ATTN_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required           */
   ATTN_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed           */
-  ATTN_ERR_NO_DEVICE = -6    /* no HIP device is visible                             */
+  ATTN_ERR_NO_DEVICE = -6,   /* no HIP device is visible                             */
+  ATTN_ERR_SCRATCH_LIMIT = -7 /* request needs more than the static scratch of
+                                 attn_decode_paged_noalloc                            */
 } attn_status;
+
+/* Size of the static device scratch array that attn_decode_paged_noalloc
+ * uses in place of a caller workspace (one copy per GPU, held until the
+ * process ends). */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES (16u << 20)
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);
@@ -183,6 +192,32 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       int kv_layout, void* o, float* lse, int num_seqs, int Hq, int Hkv, int D,
                       int num_blocks, int max_blocks_per_seq, float scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_decode_paged_noalloc - attn_decode_paged for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and result as
+ * attn_decode_paged (the same kernels run), without the workspace: the
+ * split-KV partial results go to a static device array inside the library,
+ * ATTN_DECODE_STATIC_SCRATCH_BYTES per GPU, whose address is looked up once
+ * per device on the first call made with that device current.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *   A request whose attn_decode_workspace_bytes(num_seqs, Hq, D,
+ *   max_blocks_per_seq, 16) exceeds ATTN_DECODE_STATIC_SCRATCH_BYTES is
+ *   rejected with ATTN_ERR_SCRATCH_LIMIT before anything is enqueued (e.g.
+ *   64 sequences x 32 query heads x D = 128 fit with up to 7680 tokens,
+ *   480 blocks of 16, per table row).
+ * Every call on one GPU shares that GPU's array, and each call overwrites
+ * the part it uses before reading it: calls that can overlap on one GPU
+ * (different streams without ordering between them) race on it and must be
+ * serialised by the caller.  Other errors as attn_decode_paged, except that
+ * ATTN_ERR_WORKSPACE does not occur.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int block_size, int kv_layout, void* o, float* lse, int num_seqs,
+                              int Hq, int Hkv, int D, int num_blocks, int max_blocks_per_seq,
+                              float scale, hipStream_t stream);
 
 /* Paged decode with block skipping ("高效部署稀疏注意力加速方案：BLASST方法详解与
  * 实践指南", 架构与组件: a running maximum from the blockwise online softmax and

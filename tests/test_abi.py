@@ -26,7 +26,7 @@ def test_header_lists_the_entry_points():
     names = _declared()
     for need in ("attn_prefill", "attn_prefill_f32", "attn_prefill_blockskip",
                  "attn_decode_paged", "attn_decode_paged_blockskip", "attn_prefill_paged",
-                 "attn_decode_paged_fp8",
+                 "attn_decode_paged_fp8", "attn_decode_paged_noalloc",
                  "attn_decode_workspace_bytes", "attn_status_string", "attn_arch_supported"):
         assert need in names
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_arch_names():
     assert A.attn_status_string(0) == "ok"
-    for st in (-1, -2, -3, -4, -5, -6):
+    for st in (-1, -2, -3, -4, -5, -6, -7):
         assert A.attn_status_string(st) not in ("ok", "unknown status")
     assert A.attn_status_string(7) == "unknown status"
     assert A.attn_arch_supported("gfx950")
@@ -116,6 +116,43 @@ def test_decode_workspace_and_validation_without_device():
     assert call(ws=None) == -4
     assert call(wsb=need - 1) == -4
     assert call(ws=260) == -4                # misaligned workspace
+
+
+def test_decode_noalloc_validation_without_device():
+    """The allocation-free decode validates like attn_decode_paged and rejects
+    a request whose split-KV scratch exceeds the static array, before any HIP
+    call."""
+    lib = A.load()
+    hdr = open(HEADER).read()
+    assert re.search(r"#define ATTN_DECODE_STATIC_SCRATCH_BYTES \(16u << 20\)", hdr)
+    assert A.DECODE_STATIC_SCRATCH_BYTES == 16 << 20
+
+    def call(**kw):
+        a = dict(q=8, kp=8, vp=8, bt=8, sl=8, bs=16, lay=1, o=8, N=2, Hq=8, Hkv=2, D=128, NB=8,
+                 MB=4, scale=0.1)
+        a.update(kw)
+        return lib.attn_decode_paged_noalloc(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["bs"],
+                                             a["lay"], a["o"], None, a["N"], a["Hq"], a["Hkv"],
+                                             a["D"], a["NB"], a["MB"], a["scale"], None)
+    assert call(bt=None) == -1
+    assert call(N=0) == -1
+    assert call(Hq=6, Hkv=4) == -1
+    assert call(lay=2) == -1
+    assert call(bs=32) == -2
+    assert call(D=80) == -2
+    # 64 sequences x 32 heads x D=128: rows of up to 480 blocks (15 splits of
+    # 512 tokens, 64*32*15*129*4 B) fit in 16 MiB, 481 blocks and more do not
+    lim = A.DECODE_STATIC_SCRATCH_BYTES
+    assert A.attn_decode_workspace_bytes(64, 32, 128, 480, 16) <= lim
+    assert A.attn_decode_workspace_bytes(64, 32, 128, 481, 16) > lim
+    for mb in (256, 480, 481, 512, 1024):
+        need = A.attn_decode_workspace_bytes(64, 32, 128, mb, 16)
+        st = call(N=64, Hq=32, Hkv=8, MB=mb)
+        if need > lim:
+            assert st == -7, (mb, need)
+        else:
+            assert st not in (-7, -4, -1, -2), (mb, need, st)
+    assert "static decode scratch" in A.attn_status_string(-7)
 
 
 def test_decode_blockskip_validation_without_device():
