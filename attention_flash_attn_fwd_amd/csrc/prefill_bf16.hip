@@ -39,9 +39,16 @@
 //  * A workgroup runs one to four work items (query blocks) back to back;
 //    each item's last phase writes its output through LDS as whole rows and
 //    copies the next item's Q and first two K/V tiles.
+//  * Block skip: after the row maxima of a tile each wave votes whether its
+//    rows are negligible; a 64x64 tile both of whose waves vote so loses its
+//    exponentials and its P.V, and the V tile is copied from memory only if
+//    some 64-row tile of the workgroup keeps it (P.V runs one tile later to
+//    give that copy time to land).
 #include "attn_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -126,6 +133,20 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most n (wave-uniform, 0..15) vector-memory operations of
+// this wave are in flight; a larger n waits for all of them.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+#define ATTN_WAIT_CASE(k) \
+  case k: wait_vmem<k>(); break;
+    ATTN_WAIT_CASE(1) ATTN_WAIT_CASE(2) ATTN_WAIT_CASE(3) ATTN_WAIT_CASE(4) ATTN_WAIT_CASE(5)
+    ATTN_WAIT_CASE(6) ATTN_WAIT_CASE(7) ATTN_WAIT_CASE(8) ATTN_WAIT_CASE(9) ATTN_WAIT_CASE(10)
+    ATTN_WAIT_CASE(11) ATTN_WAIT_CASE(12) ATTN_WAIT_CASE(13) ATTN_WAIT_CASE(14) ATTN_WAIT_CASE(15)
+#undef ATTN_WAIT_CASE
+    default: wait_vmem<0>(); break;
+  }
+}
+
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -152,6 +173,13 @@ struct Tile {
   static constexpr int STAGE = KT + VT;
   static constexpr int NST = 4;               // LDS stages: t-1 (role B), t, t+1, t+2 in flight
   static constexpr size_t lds_bytes = (size_t)NST * STAGE;
+  // Block skip: K and V in rings of their own, K tile t in K stage t % 4 and
+  // V tile t in V stage t % 3 (a V tile is only copied once it is known to
+  // be needed, see the block-skip loop).
+  static constexpr int VPW = VSL / 4;         // V copy blocks per wave of the copying group
+  static_assert(VSL % 4 == 0, "a V tile splits evenly over four waves");
+  static constexpr int VST = 3;
+  static constexpr size_t skip_lds_bytes = (size_t)NST * KT + VST * VT;
 };
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -182,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-  __shared__ int vote_lds[2][kWaves];  // block skip: (tile << 1) | negligible
+  __shared__ __attribute__((aligned(16))) int vote_lds[2][kWaves];  // block skip: (tile << 1) | negligible
   __shared__ unsigned char skip_lds[kWaves][256];  // block skip: decisions, 256 tiles a row
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -260,6 +288,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     const size_t kvbase = ((size_t)b * p.Hkv + kvh) * (size_t)S * D;
     const uint16_t* Kg = p.k + kvbase;
     const uint16_t* Vg = p.v + kvbase;
+    // LDS byte offsets of K tile t and V tile t (dense: one ring of K+V
+    // stages continuing across items; block skip: separate K and V rings)
+    auto k_stage = [&](int t) -> uint32_t {
+      return SKIP ? (uint32_t)(t & 3) * T::KT : (uint32_t)((t + ring) % T::NST) * T::STAGE;
+    };
+    auto v_stage = [&](int t) -> uint32_t {
+      return SKIP ? (uint32_t)(T::NST * T::KT + (t % T::VST) * T::VT)
+                  : (uint32_t)((t + ring) % T::NST) * T::STAGE + T::KT;
+    };
 
     // ---- asynchronous global -> LDS copy of tile t into stage t % NST.
     // One wave-wide load fills 1 KiB of LDS (16 bytes per lane, in lane
@@ -384,6 +421,79 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         issue_dense(Kg, Vg, t, ring);
       }
     };
+    // Block skip: K and V tiles are copied separately, each by one wave
+    // group and dealt round robin to its four waves: group 1 copies every K
+    // tile (tile j+3 in its VALU phase j), the group that copies a V tile is
+    // chosen by the decisions (see vote_collect).  Slot g of a block is row
+    // g / SL, chunk g % SL, as above; keys past the end are clamped to the
+    // last key.
+    constexpr int KB_HI = (T::KSL + 3) / 4, KB_LO = T::KSL / 4;
+    const bool kb_hi = (wave & 3) < T::KSL % 4;
+    auto slot_off = [&](int g, int sl) -> uint32_t {
+      const int r = g / sl, c = g % sl;
+      return (uint32_t)r * T::RB + (c < T::CH ? c : 0) * 16;
+    };
+    // a wave's own copy offsets: K blocks in group 1, V blocks in group 0
+    // (group 1 copies a V tile only when group 0 does not need it, and then
+    // forms the offsets as it goes)
+    constexpr int NOFF = KB_HI > T::VPW ? KB_HI : T::VPW;
+    uint32_t coff[SKIP ? NOFF : 1];
+    if constexpr (SKIP) {
+#pragma unroll
+      for (int j = 0; j < NOFF; ++j)
+        coff[j] = slot_off(((wave & 3) + 4 * j) * 64 + lane, grp == 1 ? T::KSL : T::VSL);
+    }
+    // offset of slot g of a block array with sl slots per row, with rows past
+    // lim clamped to row lim
+    auto clamp_off = [&](uint32_t o, int g, int sl, int lim) -> uint32_t {
+      const int r = g / sl;
+      return o - (uint32_t)(r - min(r, lim)) * T::RB;
+    };
+    // (whole: the caller knows that tile t has all BN keys)
+    auto issue_k = [&](int t, bool whole) {  // a group-1 wave's blocks of K tile t
+      const uint32_t st = smem_base + k_stage(t);
+      const int key0 = t * BN;
+      const uint16_t* src = Kg + (size_t)key0 * D;
+      if (whole || key0 + BN <= S) {
+#pragma unroll
+        for (int j = 0; j < KB_HI; ++j) {
+          if (j == KB_LO && !kb_hi) break;
+          dma16(src, coff[j], st + ((wave & 3) + 4 * j) * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KB_HI; ++j) {
+          if (j == KB_LO && !kb_hi) break;
+          const int i = (wave & 3) + 4 * j;
+          dma16(src, clamp_off(coff[j], i * 64 + lane, T::KSL, S - 1 - key0), st + i * 1024);
+        }
+      }
+    };
+    auto issue_v = [&](int t, bool whole) {  // this wave's VPW blocks of V tile t (its group copies it)
+      const uint32_t st = smem_base + v_stage(t);
+      const int key0 = t * BN;
+      const uint16_t* src = Vg + (size_t)key0 * D;
+      if (grp == 0 && (whole || key0 + BN <= S)) {
+#pragma unroll
+        for (int j = 0; j < T::VPW; ++j) dma16(src, coff[j], st + ((wave & 3) + 4 * j) * 1024);
+      } else {
+#pragma unroll
+        for (int j = 0; j < T::VPW; ++j) {
+          const int i = (wave & 3) + 4 * j, g = i * 64 + lane;
+          dma16(src, clamp_off(slot_off(g, T::VSL), g, T::VSL, S - 1 - key0), st + i * 1024);
+        }
+      }
+    };
+    auto issue_v_all = [&](int t) {  // every block of V tile t, from this wave
+      const uint32_t st = smem_base + v_stage(t);
+      const int key0 = t * BN;
+      const uint16_t* src = Vg + (size_t)key0 * D;
+      for (int i = 0; i < T::VSL; ++i) {
+        const int g = i * 64 + lane;
+        dma16(src, clamp_off(slot_off(g, T::VSL), g, T::VSL, S - 1 - key0), st + i * 1024);
+      }
+    };
+
     // wait until only the DMA blocks of the newest tile are in flight
     auto wait_all_but_newest = [&]() {
       if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO>(); else wait_vmem<DMA_HI>();
@@ -404,8 +514,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       // wait the compiler can see (vmcnt(0)) completes all of them, so it
       // places no vector-memory waits of its own inside the loop, where they
       // would also drain the tile prefetches.
-      issue(0);
-      if (n_tiles > 1) issue(1);
+      if constexpr (SKIP) {
+        if (grp == 1) {
+          issue_k(0, false);
+          if (n_tiles > 1) issue_k(1, false);
+        }
+      } else {
+        issue(0);
+        if (n_tiles > 1) issue(1);
+      }
       __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
       // Q (in this wave's output slice of the previous item) and tiles 0 and
@@ -436,12 +553,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     float l = 0.f;
     unsigned skipped = 0;
     const float sl2 = p.sl2;
+    const float thr = p.thr;  // block skip: log2(lambda)
     const int first_masked = CAUSAL ? min((off + q0) / BN, S / BN) : S / BN;
 
     // S^T of key tile t (raw scores) = K Q^T: two independent 32-key
     // accumulator chains, operand reads running ahead of the MFMAs
     auto qk = [&](int t, f32x16* sc) {
-      const LDS_AS unsigned char* kp = smem + ((t + ring) % T::NST) * T::STAGE + k_base;
+      const LDS_AS unsigned char* kp = smem + k_stage(t) + k_base;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[0][i] = sc[1][i] = 0.f;
 #pragma unroll
@@ -489,15 +607,35 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // softmax of a score tile into bf16 P (packed for the P.V MFMA).  The
     // exponent reference moves (with a rescale of O and l) only when the row
     // max grew by more than 8, a factor 256; the result is exact after 1/l.
+    // With block skip, P.V runs a tile later than the softmax (below), so
+    // when the reference moves, the P of the previous tile is still on its
+    // way into acc: the rescale of acc is then held (alpha_pend) and applied
+    // at the start of the next VALU phase, once that P.V has been added.
+    float alpha_pend = 1.f;
+    bool pend = false;
+    auto apply_pending = [&]() {
+      if (pend) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha_pend;
+        pend = false;
+      }
+    };
     auto softmax = [&](f32x16* sc, float tmx, uint32_t (*pk)[8]) {
       if (__any(tmx > m_used + 8.f)) {
         const float m_new = fmaxf(m_used, tmx);
         const float alpha = fast_exp2(m_used - m_new);
         l *= alpha;
+        if constexpr (SKIP) {
+          alpha_pend = alpha;
+          pend = true;
+        } else {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
         m_used = m_new;
       }
       const float nm = -m_used;
@@ -519,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // O^T += V^T P^T for key tile t; V^T fragments come from the transposing
     // LDS read, running ahead of the MFMAs
     auto pv = [&](int t, uint32_t (*pk)[8]) {
-      const LDS_AS unsigned char* vl = smem + ((t + ring) % T::NST) * T::STAGE + T::KT + v_base;
+      const LDS_AS unsigned char* vl = smem + v_stage(t) + v_base;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -548,19 +686,28 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     };
     // block skip: this wave's vote on key tile t (are all 32 of its rows
-    // negligible?), published in LDS.  The other wave of the 64-row tile runs
-    // the same phase, so its vote on t arrives within a few instructions;
-    // vote_collect waits for it (bounded; past the bound the tile is kept).
-    // The copy issue sits between the two, hiding the LDS round trip.  One
-    // wave of the pair records the decisions on its live tiles, first in an
-    // LDS row of 256 tiles, written to the bitmap when the row is full and
-    // at the end (a store per tile cost 8%).  vote_collect is true if tile t
-    // is skipped.
+    // negligible?), published in LDS.  The other waves of the wave group run
+    // the same phase, so their votes on t arrive within a few instructions;
+    // vote_collect waits for the group's four (the other wave of this
+    // wave's 64-row tile is among them).  The copy issue sits between
+    // publish and collect, hiding the LDS round trip.  V tile t is copied by
+    // group 0 if one of its 64-row tiles keeps t, else by group 1 if one of
+    // its tiles does (group 1 runs its phase after group 0's and sees group
+    // 0's votes); it is not copied at all when every tile of the workgroup
+    // skips t.  The wait is bounded: a wave whose group's votes do not all
+    // arrive keeps the tile (always exact), republishes its own vote as
+    // "keep" before the phase's closing barrier (so group 1 knows that group
+    // 0 needs the tile), and copies the whole V tile itself (lost = true).
+    // One wave of each 64-row tile records the decisions on its live tiles,
+    // first in an LDS row of 256 tiles, written to the bitmap when the row is
+    // full and at the end (a store per tile cost 8%).  vote_collect is true
+    // if tile t is skipped; copyv says whether this wave's group copies V
+    // tile t.
     const bool records = SKIP && ((slot / p.gw) & 1) == 0;
-    auto vote_publish = [&](int t, float tmx_t) -> bool {
+    auto vote_publish = [&](int t, float tmx_t, bool live) -> bool {
       bool neg = true;
-      if (t < wave_tiles)
-        neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < p.thr) ||
+      if (live)
+        neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < thr) ||
               (q0 + n >= S);
       const bool all_neg = __all(neg);
       if (lane == 0)
@@ -568,14 +715,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
                            __HIP_MEMORY_SCOPE_WORKGROUP);
       return all_neg;
     };
-    auto vote_collect = [&](int t, bool all_neg) -> bool {
-      int other = -1;
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    // lanes 0-7 each read one wave's vote; ballots then test the tags and
+    // gather the verdicts (bit w = wave w)
+    const uint32_t vote_lane = lane < kWaves ? lane : 0;
+    const uint64_t grp_mask = grp == 0 ? 0x0Full : 0xFFull;  // group 1 also waits for group 0's votes
+    auto vote_collect = [&](int t, bool all_neg, bool& copyv, bool& lost) -> bool {
+      int v = 0;
+      bool got = false;
       for (int spin = 0; spin < (1 << 16); ++spin) {
-        other = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-            &vote_lds[t & 1][pwave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if ((other >> 1) == t) break;
+        v = *(volatile LDS_AS int*)(&vote_lds[t & 1][vote_lane]);
+        if ((__ballot((v >> 1) == t) & grp_mask) == grp_mask) { got = true; break; }
       }
-      const bool sk = all_neg && (other >> 1) == t && (other & 1);
+      lost = !got;
+      const uint64_t keeps = __ballot(!(v & 1));   // waves with a row that keeps t
+      const bool need0 = (keeps & 0x0Full) != 0, need1 = (keeps & 0xF0ull) != 0;
+      // does a 64-row tile of group 0 keep t?  then group 0 copies V tile t;
+      // else group 1 does if one of its tiles keeps it
+      copyv = grp == 0 ? need0 : (need1 && !need0);
+      const bool other_neg = ((keeps >> pwave) & 1) == 0;
+      if (__builtin_expect(lost, 0)) {
+        // the wait ran out: keep the tile, say so, and copy V tile t
+        copyv = true;
+        if (lane == 0)
+          __hip_atomic_store(&vote_lds[t & 1][wave], t << 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      const bool sk = got && all_neg && other_neg;
       if (records && t < wave_tiles) {
         if (lane == 0) skip_lds[wave][t & 255] = sk ? 1 : 0;
         skipped += sk ? 1u : 0u;
@@ -627,7 +794,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       const float lt = half_swap_add(l);
       const float inv = 1.f / lt;
       static_assert(4 * 32 * D * 2 <= T::STAGE, "four output slices must fit in a stage");
-      const uint32_t slice = ((ring + n_tiles + 2 + grp) % T::NST) * T::STAGE + (wave & 3) * (32 * D * 2);
+      static_assert(2 * 4 * 32 * D * 2 <= T::NST * T::KT, "eight output slices must fit in the K ring");
+      // block skip: group g's slices in the K ring, free once the last Q.K^T is done
+      const uint32_t slice = (SKIP ? (uint32_t)grp * (4 * 32 * D * 2)
+                                   : ((ring + n_tiles + 2 + grp) % T::NST) * T::STAGE) +
+                             (wave & 3) * (32 * D * 2);
       LDS_AS unsigned char* ost = smem + slice;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -739,75 +910,99 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       for (; j < n_tiles; ++j) general(j);
       finish(n_tiles - 1 < wave_tiles, pk);
     } else {
-      // Block skip, in the same ping-pong.  In its VALU phase j a wave takes
-      // the row maxima of tile j, votes, and waits for the vote of the other
-      // wave of the 64-row tile (same group, same phase).  A skipped tile loses
-      // its softmax now and its P.V in the next MFMA phase; the running max of
-      // the decisions (m_true) takes every tile, skipped or not.
-      uint32_t pk[2][8];
-      bool skip_prev = false;
+      // Block skip, in the same ping-pong, with the V load gated on the
+      // decisions.  In its VALU phase j a wave takes the row maxima of tile
+      // j and votes; a skipped tile loses its softmax there and its P.V
+      // later; the running max of the decisions (m_true) takes every tile,
+      // skipped or not.  V tile j is copied in that phase by a group that
+      // keeps it (vote_collect), so it is known to be needed before it is
+      // loaded.  To give that copy a full phase pair to land, P.V of tile j
+      // runs in MFMA phase j+2 (not j+1): the P of two tiles are held (pkA
+      // for even tiles, pkB for odd ones), V tiles sit in a three-stage ring
+      // (V tile j overwrites tile j-3, whose last reader finished in MFMA
+      // phase j-1), and the copying group waits for them at the end of its
+      // VALU phase j+1.  K tiles sit in their own four-stage ring; group 1
+      // copies tile j+3 in its VALU phase j and waits for it at the end of
+      // its VALU phase j+1, before either group's Q.K^T of it.  In the
+      // common case of a tile both groups keep, group 0 copies its V and
+      // group 1 the K of a later tile, so the two phases issue about the
+      // same number of copies.
+      uint32_t pkA[2][8], pkB[2][8];
+      bool keepA = false, keepB = false;  // P.V due for the tile whose P is in pkA / pkB
       if (lane == 0) {
         vote_lds[0][wave] = -2;
         vote_lds[1][wave] = -2;
       }
       block_barrier();
       if (grp == 1) {
-        if (2 < n_tiles) issue(2);
+        if (2 < n_tiles) issue_k(2, false);
         block_barrier();
       }
-      // wait for the copies before the newest, with this phase's bitmap store
-      // (issued after them) left in flight as well
-      // the copy wait of a phase whose four bitmap stores follow its copies
-      auto wait_copies_flushed = [&]() {
-        if (DMA_HI == DMA_LO || !dma_hi) wait_vmem<DMA_LO + 4>(); else wait_vmem<DMA_HI + 4>();
-      };
-      auto general = [&](int j) {
-        if (j >= 1 && j - 1 < wave_tiles && !skip_prev) pv(j - 1, pk);
-        if (j < wave_tiles) qk(j, sc);
+      // one phase pair; pk holds the P of tile j-2 (read in the MFMA phase)
+      // and receives that of tile j; keep likewise.  STEADY: every step is
+      // present and no mask is needed (the steady-state copy of the body).
+      auto phase = [&](int j, uint32_t (*pk)[8], bool& keep, auto steady_tag) {
+        constexpr bool STEADY = decltype(steady_tag)::value;
+        if (STEADY ? keep : (j >= 2 && keep)) pv(j - 2, pk);
+        if (STEADY || j < wave_tiles) qk(j, sc);
         block_barrier();
-        const bool issues = j + 2 + grp < n_tiles;
-        float tmx = -INFINITY;
-        bool mine = false;
-        if (j < n_tiles) {
-          if (j < wave_tiles) tmx = row_max(j, sc);
-          mine = vote_publish(j, tmx);
-        }
-        if (issues) issue(j + 2 + grp);
-        const bool flush = flush_due(j);
-        if (j < n_tiles) {
-          const bool sk = vote_collect(j, mine);
-          if (flush) flush_skips(j - 255);
+        apply_pending();
+        int inflight = 0;  // vector-memory operations issued in this phase
+        keep = false;
+        if (STEADY || j < n_tiles) {
+          const float tmx = STEADY ? tile_max(sc) : (j < wave_tiles ? row_max(j, sc) : -INFINITY);
+          const bool mine = vote_publish(j, tmx, STEADY || j < wave_tiles);
+          if (grp == 1 && (STEADY || j + 3 < n_tiles)) {
+            issue_k(j + 3, STEADY);
+            inflight += kb_hi ? KB_HI : KB_LO;
+          }
+          bool copyv, lost;
+          const bool sk = vote_collect(j, mine, copyv, lost);
+          if (flush_due(j)) {
+            flush_skips(j - 255);
+            inflight += 4;
+          }
+          if (copyv) {
+            if (__builtin_expect(lost, 0)) {
+              issue_v_all(j);
+              wait_vmem<0>();
+              inflight = 0;
+            } else {
+              issue_v(j, STEADY);
+              inflight += T::VPW;
+            }
+          }
           m_true = fmaxf(m_true, tmx);
-          if (j < wave_tiles && !sk) softmax(sc, tmx, pk);
-          skip_prev = sk;
+          keep = (STEADY || j < wave_tiles) && !sk;
+          if (keep) softmax(sc, tmx, pk);
         }
-        if (!issues) wait_vmem<0>();
-        else if (flush) wait_copies_flushed();
-        else wait_all_but_newest();
+        wait_vmem_upto(inflight);
         block_barrier();
       };
-      general(0);
-      // steady iterations: every step present, no mask (as in the dense loop)
-      const int j_ss = max(1, min(min(wave_tiles, first_masked), n_tiles - 3));
-      int j = 1;
-      for (; j < j_ss; ++j) {
-        if (!skip_prev) pv(j - 1, pk);
-        qk(j, sc);
-        block_barrier();
-        const float tmx = tile_max(sc);
-        const bool mine = vote_publish(j, tmx);
-        issue(j + 2 + grp);
-        const bool sk = vote_collect(j, mine);
-        const bool flush = flush_due(j);
-        if (flush) flush_skips(j - 255);
-        m_true = fmaxf(m_true, tmx);
-        if (!sk) softmax(sc, tmx, pk);
-        skip_prev = sk;
-        if (flush) wait_copies_flushed(); else wait_all_but_newest();
-        block_barrier();
+      using Gen = std::integral_constant<bool, false>;
+      using Ste = std::integral_constant<bool, true>;
+      // steady phases: 2 <= j < j_ss (P.V of j-2, Q.K^T of j, the K copy of
+      // tile j+3, no mask, and K tile j+3 and V tile j not the last tile, so
+      // whole), run in pairs so that each P buffer stays in fixed registers
+      const int j_ss = min(min(wave_tiles, first_masked), n_tiles - 4);
+      phase(0, pkA, keepA, Gen{});
+      if (1 <= n_tiles) phase(1, pkB, keepB, Gen{});
+      int j = 2;
+      for (; j + 1 < j_ss; j += 2) {
+        phase(j, pkA, keepA, Ste{});
+        phase(j + 1, pkB, keepB, Ste{});
       }
-      for (; j < n_tiles; ++j) general(j);
-      finish(n_tiles - 1 < wave_tiles && !skip_prev, pk);
+      for (; j <= n_tiles; j += 2) {
+        phase(j, pkA, keepA, Gen{});
+        if (j + 1 <= n_tiles) phase(j + 1, pkB, keepB, Gen{});
+      }
+      // MFMA phase n_tiles + 1: P.V of the last tile
+      if ((n_tiles + 1) & 1) {
+        if (keepB) pv(n_tiles - 1, pkB);
+      } else {
+        if (keepA) pv(n_tiles - 1, pkA);
+      }
+      finish(false, pkA);
     }
 
     if (!has_next()) break;
@@ -819,15 +1014,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
 template <int D, bool CAUSAL, bool SKIP, bool PAGED = false>
 hipError_t launch_one(const Params& p, int grid, hipStream_t stream) {
   auto kern = prefill_bf16_kernel<D, CAUSAL, SKIP, PAGED>;
+  constexpr size_t lds = SKIP ? Tile<D>::skip_lds_bytes : Tile<D>::lds_bytes;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)Tile<D>::lds_bytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), Tile<D>::lds_bytes, stream, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 

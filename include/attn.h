@@ -127,6 +127,9 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o, f
  * (m_r is defined and tm_r - m_r < ln(lambda)); the tile is skipped (no exp,
  * no P.V, no update of the row statistics) iff all of its rows are negligible.
  * O and LSE are then exact attention over the keys of the tiles not skipped.
+ * The V rows of key tile kt are not read from memory when every query tile
+ * processed together with it (up to four query heads of the K/V group, 64
+ * rows each) skips kt.
  *
  *   lambda        : 0 < lambda < 1
  *   tile          : must be 64
