@@ -256,9 +256,9 @@ int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int total_q, 
   if (Hkv > 65535) return ATTN_ERR_UNSUPPORTED;  // pool block bytes stay 32-bit
   int st = check_device();
   if (st != ATTN_OK) return st;
-  attn::PagedPrefillArgs a{q, cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k, o, lse,
-                           num_seqs, Hq, Hkv, D, num_blocks, max_blocks_per_seq, max_seqlen_q,
-                           scale};
+  attn::PagedPrefillArgs a{q,     cu_seqlens_q, k_pool, v_pool, block_table, seq_lens_k,
+                           o,     lse,          num_seqs, Hq,    Hkv,         D,
+                           num_blocks, max_blocks_per_seq, max_seqlen_q, total_q, scale};
   return hip_status(attn::launch_prefill_paged(a, stream));
 }
 

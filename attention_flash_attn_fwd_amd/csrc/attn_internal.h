@@ -38,7 +38,7 @@ struct PagedPrefillArgs {
   const int32_t* seq_lens_k;  // [N]
   void* o;                    // bf16 [total_q, Hq, D]
   float* lse;                 // [total_q, Hq] or null
-  int N, Hq, Hkv, D, num_blocks, max_blocks, max_seqlen_q;
+  int N, Hq, Hkv, D, num_blocks, max_blocks, max_seqlen_q, total_q;
   float scale;
 };
 

@@ -82,7 +82,7 @@ struct Params {
   const int32_t* cu_q;     // [N + 1] query offsets into the packed q / o / lse
   const int32_t* seq_k;    // [N] cached tokens per sequence (Sk)
   const int32_t* table;    // [N, max_blocks] block table
-  int N, max_blocks, num_blocks;
+  int N, max_blocks, num_blocks, total_q, max_seqlen_q;
   // work items (query block x head group) and how many each workgroup runs
   int n_items, items_per_wg;
 };
@@ -257,22 +257,41 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // Sq query rows at key positions off .. off+Sq-1 of Sk keys (dense: all S)
     int Sq = p.S, Sk = p.S, off = 0, qstart = 0;
     if constexpr (PAGED) {
-      qstart = p.cu_q[seq];
-      Sq = p.cu_q[seq + 1] - qstart;
+      // The sequence's device-side description is checked before anything
+      // is read through it: query offsets inside [0, total_q] and in order,
+      // at most max_seqlen_q queries (the grid's reach), Sq <= Sk <= the
+      // table row, and every table entry its keys use inside the pool.  A
+      // sequence that breaks any of these gets NaN in O and LSE for its
+      // rows, clamped to [0, total_q), and nothing else is read or written.
+      const int lo = p.cu_q[seq], hi = p.cu_q[seq + 1];
       Sk = p.seq_k[seq];
-      off = Sk - Sq;
-      if (row0 >= Sq) return;  // whole workgroup past this chunk
-      if (Sq < 0 || off < 0 || Sk > p.max_blocks * 16) {
-        // lengths that do not fit the table: NaN rows, nothing read
-        const int row = q0 + n;
-        if (row < Sq) {
-          uint16_t* orow = p.o + ((size_t)(qstart + row) * p.Hq + head) * D;
+      bool bad = lo < 0 || hi > p.total_q || hi < lo || hi - lo > p.max_seqlen_q || Sk < 0 ||
+                 Sk > p.max_blocks * 16 || hi - lo > Sk;
+      if (!bad) {
+        const int32_t* trow = p.table + (size_t)seq * p.max_blocks;
+        bool bad_entry = false;
+        for (int x = lane; x < (Sk + 15) >> 4; x += 64) {
+          const int e = trow[x];
+          bad_entry = bad_entry || e < 0 || e >= p.num_blocks;
+        }
+        bad = __any(bad_entry);
+      }
+      if (bad) {
+        // every workgroup of the sequence covers its query block and the
+        // blocks n_qblk, 2 n_qblk, ... after it, so all rows get NaN
+        const int r_lo = max(lo, 0), r_hi = min(hi, p.total_q);
+        for (int row = r_lo + q0 + n; row < r_hi; row += p.n_qblk * p.rows_per_wg) {
+          uint16_t* orow = p.o + ((size_t)row * p.Hq + head) * D;
           for (int d = hf * 4; d < D; d += 8)
             *reinterpret_cast<u32x2*>(orow + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-          if (hf == 0 && p.lse) p.lse[(size_t)(qstart + row) * p.Hq + head] = NAN;
+          if (hf == 0 && p.lse) p.lse[(size_t)row * p.Hq + head] = NAN;
         }
         return;
       }
+      qstart = lo;
+      Sq = hi - lo;
+      off = Sk - Sq;
+      if (row0 >= Sq) return;  // whole workgroup past this chunk
     }
     const int S = Sk;  // key count
 
@@ -1097,6 +1116,8 @@ hipError_t launch_prefill_paged(const PagedPrefillArgs& a, hipStream_t stream) {
   p.N = a.N;
   p.max_blocks = a.max_blocks;
   p.num_blocks = a.num_blocks;
+  p.total_q = a.total_q;
+  p.max_seqlen_q = a.max_seqlen_q;
   const long long grid = (long long)p.n_qblk * a.N * p.n_hgrp;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const int g = (int)grid;

@@ -292,11 +292,14 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
  *                   ([num_blocks, Hkv, 16, D]; ATTN_ERR_UNSUPPORTED otherwise)
  *   block_table   : int32 [num_seqs, max_blocks_per_seq]
  * Hkv above 65535 gives ATTN_ERR_UNSUPPORTED, as in the decode.
- * Requirements on the device data (not checked on the host): Sq <= Sk and
- * Sk <= 16 * max_blocks_per_seq (a sequence breaking them gets NaN rows),
- * Sq <= max_seqlen_q, valid table entries (out-of-range entries are
- * clamped into the pool: the result is then unspecified, no read leaves
- * the pool). */
+ * Device-side values are checked by the kernel before anything is read
+ * through them.  A sequence n with cu_seqlens_q[n] < 0, cu_seqlens_q[n+1] >
+ * total_q, cu_seqlens_q[n+1] < cu_seqlens_q[n], Sq > max_seqlen_q, Sq > Sk,
+ * Sk < 0, Sk > 16 * max_blocks_per_seq, or a table entry outside
+ * [0, num_blocks) among the ceil(Sk/16) blocks it uses gets NaN in O and LSE
+ * for its rows [max(cu[n], 0), min(cu[n+1], total_q)) (none if that range is
+ * empty); no other row is written and no memory outside q, the pools, the
+ * table and the offsets is read. */
 int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int total_q, int max_seqlen_q,
                        const void* k_pool, const void* v_pool, const int32_t* block_table,
                        const int32_t* seq_lens_k, int block_size, int kv_layout, void* o,

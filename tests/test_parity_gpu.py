@@ -280,6 +280,42 @@ def test_prefill_paged_varlen(Hq, Hkv, D):
     _compare(o, lse, ro, rl, TOL["bf16"], "paged prefill")
 
 
+def test_prefill_paged_bad_device_values_give_nan_rows_only():
+    """Malformed device-side descriptions poison only their own rows, with
+    bounded writes: a table entry out of the pool (sequence 1), more queries
+    than max_seqlen_q (sequence 2), a last query offset past total_q
+    (sequence 3).  Guard rows around O and LSE stay untouched; the good
+    sequence matches the oracle."""
+    say("chunked paged prefill: bad table entry, Sq > max_seqlen_q, cu_seqlens_q past total_q")
+    ctx, ql = [100, 50, 200, 30], [40, 64, 100, 20]
+    d = paged_prefill_inputs(ctx, ql, 8, 2, 128, seed=140, tail="nan")
+    total_q = int(d.cu_seqlens_q[-1])
+    cu = d.cu_seqlens_q.clone()
+    cu[4] = total_q + 5
+    bt = d.block_table.clone()
+    bt[1, 2] = d.num_blocks + 3
+    G = 7
+    o_big = torch.empty((total_q + 2 * G, 8, 128), dtype=torch.bfloat16, device="cuda")
+    o_big.view(torch.int16).fill_(0x1234)
+    l_big = torch.full((total_q + 2 * G, 8), 123.0, dtype=torch.float32, device="cuda")
+    o, lse = o_big[G:G + total_q], l_big[G:G + total_q]
+    A.attn_prefill_paged(d.q.cuda(), cu.cuda(), d.k_pool.cuda(), d.v_pool.cuda(), bt.cuda(),
+                         d.seq_lens_k.cuda(), o, lse, 64, d.scale)
+    torch.cuda.synchronize()
+    ob = o_big.view(torch.int16).cpu()
+    lb = l_big.cpu()
+    assert (ob[:G] == 0x1234).all() and (ob[G + total_q:] == 0x1234).all(), "guard rows of O written"
+    assert (lb[:G] == 123.0).all() and (lb[G + total_q:] == 123.0).all(), "guard rows of LSE written"
+    of, lf = o.float().cpu().numpy(), lse.cpu().numpy()
+    c = d.cu_seqlens_q.numpy()
+    for n in (1, 2, 3):
+        assert np.isnan(of[c[n]:c[n + 1]]).all() and np.isnan(lf[c[n]:c[n + 1]]).all(), n
+    ro, rl = ref_prefill_paged(upcast_f64(d.q), d.cu_seqlens_q.numpy(), upcast_f64(d.k_pool),
+                               upcast_f64(d.v_pool), d.block_table.numpy(),
+                               d.seq_lens_k.numpy(), 16, d.scale)
+    _compare(of[:c[1]], lf[:c[1]], ro[:c[1]], rl[:c[1]], TOL["bf16"], "paged prefill good sequence")
+
+
 def test_prefill_paged_two_chunks_match_dense_prefill():
     say("two chunks of one sequence through the paged cache = the dense causal prefill")
     S, Hq, Hkv, D = 700, 8, 2, 128
