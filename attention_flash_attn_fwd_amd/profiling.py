@@ -1,8 +1,10 @@
-"""Helpers that turn rocprofv3 result databases into the short text and JSON
-summaries kept under profiles/.  Nothing here runs attention; it only reads
-rocprofv3's SQLite output, plus one plain copy kernel used to calibrate the
-HBM byte counters.
+"""Measurement helpers: the workload launcher profiled under rocprofv3, and
+the code that turns rocprofv3's result databases into the short text and
+JSON summaries kept under profiles/.
 
+    python -m attention_flash_attn_fwd_amd.profiling launch WORKLOAD [--reps 5] [--warmup 3]
+        run one named workload (seeded inputs, the library's entry points)
+        REPS times after WARMUP launches; the command that rocprofv3 wraps
     python -m attention_flash_attn_fwd_amd.profiling copy [--mib 1024] [--reps 5]
         run torch's elementwise copy of a MiB-sized float32 buffer REPS times
         (the calibration kernel: reads and writes exactly MiB MiB per launch)
@@ -12,6 +14,10 @@ HBM byte counters.
         --copy-fetch DB --copy-write DB --copy-mib 1024 --cmd "..." --out-json F --out-txt F
         HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch),
         each scaled by the factor that maps the copy kernel's reading to its true size
+    python -m attention_flash_attn_fwd_amd.profiling counters --dir D --copy-fetch DB
+        --copy-write DB --out-json F --out-txt F
+        per workload under D (subfolders WORKLOAD/{trace,fetch,write,mfma}), the
+        kernel time, calibrated HBM bytes and the MFMA-busy fraction per launch
 """
 from __future__ import annotations
 
@@ -158,9 +164,232 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+# ---------------------------------------------------------------- workloads
+
+# name -> (kernel-name fragment of its dominant kernel, source file, what a
+# launch computes: ("flops", n) or ("bytes", n) filled in by launch())
+WORKLOADS = ["gqa_causal_s8192", "mha_causal_s2048", "blockskip_s32768",
+             "blockskip_s32768_stress", "chunked_prefill_paged", "paged_decode_gqa",
+             "paged_decode_gqa_mfma", "paged_decode_gqa_fp8", "paged_decode_blockskip_stress"]
+KERNEL_OF = {
+    "gqa_causal_s8192": "prefill_bf16_kernel<128, true, false, false>",
+    "mha_causal_s2048": "prefill_bf16_kernel<128, true, false, false>",
+    "blockskip_s32768": "prefill_bf16_kernel<128, true, true, false>",
+    "blockskip_s32768_stress": "prefill_bf16_kernel<128, true, true, false>",
+    "chunked_prefill_paged": "prefill_bf16_kernel<128, true, false, true>",
+    "paged_decode_gqa": "decode_split_kernel<128>",
+    "paged_decode_gqa_mfma": "decode_native_kernel<128>",
+    "paged_decode_gqa_fp8": "decode_fp8_kernel<128, 2>",
+    "paged_decode_blockskip_stress": "decode_skip_kernel<128>",
+}
+SOURCE_OF = {k: ("decode_paged.hip" if k.startswith("paged") else "prefill_bf16.hip")
+             for k in WORKLOADS}
+
+
+def workload_runner(name: str):
+    """(run, work) for a named workload: run() launches it once on the
+    current stream; work = {"flops": F} (prefill, algorithmic) or
+    {"kv_bytes": B} (decode, K/V bytes that must be read)."""
+    import torch
+    import attention_flash_attn_fwd_amd as A
+    from workloads import (CONFIGS, blockskip_inputs, decode_inputs, fp8_decode_inputs,
+                           paged_prefill_inputs, prefill_flops, prefill_inputs)
+    dev = "cuda"
+    if name in ("gqa_causal_s8192", "mha_causal_s2048"):
+        c = CONFIGS[name]
+        w = prefill_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"])
+        q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((c["B"], c["Hq"], c["S"]), dtype=torch.float32, device=dev)
+        return (lambda: A.attn_prefill(q, k, v, o, lse, True, w.scale),
+                {"flops": prefill_flops(c["B"], c["Hq"], c["S"], c["D"], True)})
+    if name.startswith("blockskip_s32768"):
+        c = CONFIGS["blockskip_s32768"]
+        stress = name.endswith("stress")
+        w = blockskip_inputs(c["B"], c["Hq"], c["Hkv"], c["S"], c["D"], seed=c["seed"],
+                             amplitude=12.0 if stress else c["amplitude"],
+                             boosted="second_half" if stress else c["boosted"])
+        q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((c["B"], c["Hq"], c["S"]), dtype=torch.float32, device=dev)
+
+        def run():
+            A.attn_prefill_blockskip(q, k, v, o, lse, w.scale, c["lam"], 64, None, None)
+            if not stress:  # the dense kernel on the same inputs, for comparison
+                A.attn_prefill(q, k, v, o, lse, True, w.scale)
+        return run, {"flops": prefill_flops(c["B"], c["Hq"], c["S"], c["D"], True)}
+    if name == "chunked_prefill_paged":
+        ctx_l, q_l = [3584] * 8, [512] * 8
+        wc = paged_prefill_inputs(ctx_l, q_l, 32, 8, 128, seed=2005)
+        cq, ccu = wc.q.to(dev), wc.cu_seqlens_q.to(dev)
+        ckp, cvp = wc.k_pool.to(dev), wc.v_pool.to(dev)
+        cbt, csk = wc.block_table.to(dev), wc.seq_lens_k.to(dev)
+        co = torch.empty_like(cq)
+        clse = torch.empty((int(wc.cu_seqlens_q[-1]), 32), dtype=torch.float32, device=dev)
+        pairs = sum(qn * cx + qn * (qn + 1) // 2 for cx, qn in zip(ctx_l, q_l))
+        return (lambda: A.attn_prefill_paged(cq, ccu, ckp, cvp, cbt, csk, co, clse,
+                                             wc.max_seqlen_q, wc.scale),
+                {"flops": 4 * 32 * 128 * pairs})
+    c = CONFIGS["paged_decode_gqa"]
+    layout = "mfma" if name in ("paged_decode_gqa_mfma", "paged_decode_blockskip_stress") \
+        else "rowmajor"
+    amp = 12.0 if name == "paged_decode_blockskip_stress" else 0.0
+    d = decode_inputs(c["N"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], lmin=c["lmin"],
+                      lmax=c["lmax"], layout=layout, sink_amplitude=amp,
+                      sink_frac=1 / 64 if amp else 0.0)
+    q, bt, sl = d.q.to(dev), d.block_table.to(dev), d.seq_lens.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((c["N"], c["Hq"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(A.attn_decode_workspace_bytes(c["N"], c["Hq"], c["D"], d.max_blocks, 16),
+                     dtype=torch.uint8, device=dev)
+    if name == "paged_decode_gqa_fp8":
+        f8 = fp8_decode_inputs(c["N"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"],
+                               lmin=c["lmin"], lmax=c["lmax"])
+        pools = [(f8.k_pool.to(dev), f8.v_pool.to(dev)) for _ in range(2)]
+        ctr = [0]
+
+        def run_fp8():
+            kp, vp = pools[ctr[0] % 2]
+            ctr[0] += 1
+            A.attn_decode_paged_fp8(q, kp, vp, bt, sl, 16, o, lse, d.scale, f8.k_scale,
+                                    f8.v_scale, ws)
+        return run_fp8, {"kv_bytes": f8.kv_bytes()}
+    # two copies of the pool, used alternately, so that the 256 MB last-level
+    # cache cannot serve a launch's K/V from the previous one
+    pools = [(d.k_pool.to(dev), d.v_pool.to(dev)) for _ in range(2)]
+    ctr = [0]
+
+    def run_dec():
+        kp, vp = pools[ctr[0] % 2]
+        ctr[0] += 1
+        if amp:
+            A.attn_decode_paged_blockskip(q, kp, vp, bt, sl, 16, o, lse, d.scale, 1e-3, ws,
+                                          None, None, layout=layout)
+        else:
+            A.attn_decode_paged(q, kp, vp, bt, sl, 16, o, lse, d.scale, ws, layout=layout)
+    return run_dec, {"kv_bytes": d.kv_bytes()}
+
+
+def cmd_launch(a):
+    import torch
+    torch.cuda.set_device(0)
+    run, work = workload_runner(a.workload)
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    for _ in range(a.reps):
+        run()
+    torch.cuda.synchronize()
+    print(f"launched {a.workload}: {a.warmup} warm-up + {a.reps} timed launches; {work}",
+          flush=True)
+
+
+N_XCC = 8          # MI355X: 8 XCDs; GRBM_GUI_ACTIVE is counted on each
+N_SIMD = 1024      # 256 compute units x 4 SIMDs
+
+
+def _per_dispatch(db_path: str, counter: str, frag: str, last: int):
+    """(value, duration ns) of a counter for the last `last` dispatches of the
+    kernels whose name contains frag (rocprofv3 sums a counter over its
+    instances in counters_collection)."""
+    cur = sqlite3.connect(db_path).cursor()
+    rows = [(r[0], float(r[1]), float(r[2])) for r in cur.execute(
+        "select dispatch_id, value, duration from counters_collection "
+        "where counter_name = ? and kernel_name like ?", (counter, f"%{frag}%"))]
+    rows.sort()
+    return [(v, d) for _, v, d in rows[-last:]]
+
+
+def _last_durations(db_path: str, frag: str, last: int):
+    cur = sqlite3.connect(db_path).cursor()
+    rows = list(cur.execute("select start, duration from kernels where name like ? order by start",
+                            (f"%{frag}%",)))
+    return [float(d) for _, d in rows[-last:]]
+
+
+def cmd_counters(a):
+    ff, fk, _ = _copy_factor(a.copy_fetch, "FETCH_SIZE", a.copy_mib)
+    wf, wk, _ = _copy_factor(a.copy_write, "WRITE_SIZE", a.copy_mib)
+    rec = {"_calibration": {"copy_kernel": f"torch.neg over {a.copy_mib} MiB float32",
+                            "FETCH_SIZE_KiB": round(fk, 1), "fetch_factor": round(ff, 5),
+                            "WRITE_SIZE_KiB": round(wk, 1), "write_factor": round(wf, 5)},
+           "_commands": a.cmd_note, "_dispatches": f"the last {a.last} launches of each run"}
+    lines = ["Counters per launch of each workload's dominant kernel (rocprofv3, MI355X), over",
+             f"the last {a.last} launches of each run (earlier ones warm the chip up).", "",
+             "Commands (repo root, TMPDIR=/tmp), for each WORKLOAD:", "  " + a.cmd_note, "",
+             f"HBM bytes = FETCH_SIZE and WRITE_SIZE (KiB) x the factor that maps a "
+             f"{a.copy_mib} MiB copy's reading to its true size (fetch {ff:.4f}, write {wf:.4f}).",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs): the "
+             "share of SIMD cycles the matrix cores worked,",
+             "at the clock the chip ran (GRBM_GUI_ACTIVE per XCD / kernel time of the same "
+             "dispatch); MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / kernel time.", "",
+             f"{'workload':<30} {'trace us':>9} {'fetch MB':>9} {'write MB':>9} "
+             f"{'MFMA busy':>9} {'clock GHz':>9} {'MFMA TF/s':>9}"]
+    for wl in WORKLOADS:
+        d = os.path.join(a.dir, wl)
+        if not os.path.isdir(d):
+            continue
+        frag = KERNEL_OF[wl]
+        r = {"kernel": frag, "source": SOURCE_OF[wl],
+             "source_sha256_16": source_hash(SOURCE_OF[wl])}
+        durs = _last_durations(find_db(os.path.join(d, "trace")), frag, a.last)
+        us = sum(durs) / len(durs) / 1e3 if durs else None
+        r["kernel_us"] = round(us, 2) if us else None
+        if os.path.isdir(os.path.join(d, "fetch")):
+            v = _per_dispatch(find_db(os.path.join(d, "fetch")), "FETCH_SIZE", frag, a.last)
+            r["fetch_bytes"] = round(sum(x for x, _ in v) / len(v) * 1024 * ff) if v else None
+        if os.path.isdir(os.path.join(d, "write")):
+            v = _per_dispatch(find_db(os.path.join(d, "write")), "WRITE_SIZE", frag, a.last)
+            r["write_bytes"] = round(sum(x for x, _ in v) / len(v) * 1024 * wf) if v else None
+        if r.get("fetch_bytes") is not None and r.get("write_bytes") is not None:
+            r["bytes_per_launch"] = r["fetch_bytes"] + r["write_bytes"]
+        if os.path.isdir(os.path.join(d, "mfma")):
+            db = find_db(os.path.join(d, "mfma"))
+            b = _per_dispatch(db, "SQ_VALU_MFMA_BUSY_CYCLES", frag, a.last)
+            g = _per_dispatch(db, "GRBM_GUI_ACTIVE", frag, a.last)
+            m = _per_dispatch(db, "SQ_INSTS_VALU_MFMA_MOPS_BF16", frag, a.last)
+            if b and g:
+                busy = [x for x, _ in b]
+                gui = [x / N_XCC for x, _ in g]
+                r["mfma_busy_frac"] = round(sum(bb / (gg * N_SIMD) for bb, gg in zip(busy, gui)) /
+                                            len(gui), 4)
+                r["gui_active_cycles_per_xcd"] = round(sum(gui) / len(gui))
+                r["clock_ghz"] = round(sum(gg / dd for gg, (_, dd) in zip(gui, g)) / len(g), 3)
+                r["counter_run_kernel_us"] = round(sum(dd for _, dd in g) / len(g) / 1e3, 2)
+            if m:
+                r["mfma_flops_per_launch"] = round(sum(x for x, _ in m) / len(m) * 512)
+                r["mfma_tflops"] = round(sum(x * 512 / (dd * 1e-9) for x, dd in m) / len(m) / 1e12,
+                                         1)
+        rec[wl] = r
+
+        def f(x, k=1.0, nd=1):
+            return f"{x / k:>9.{nd}f}" if isinstance(x, (int, float)) else f"{'-':>9}"
+        lines.append(f"{wl:<30} {f(us, 1, 1)} {f(r.get('fetch_bytes'), 1e6)} "
+                     f"{f(r.get('write_bytes'), 1e6)} {f(r.get('mfma_busy_frac'), 0.01)}% "
+                     f"{f(r.get('clock_ghz'), 1, 3)} {f(r.get('mfma_tflops'), 1, 1)}")
+    with open(a.out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(a.out_txt, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sp = ap.add_subparsers(dest="cmd_name", required=True)
+    la = sp.add_parser("launch")
+    la.add_argument("workload", choices=WORKLOADS)
+    la.add_argument("--reps", type=int, default=5)
+    la.add_argument("--warmup", type=int, default=3)
+    co = sp.add_parser("counters")
+    co.add_argument("--dir", required=True)
+    co.add_argument("--copy-fetch", required=True)
+    co.add_argument("--copy-write", required=True)
+    co.add_argument("--copy-mib", type=int, default=1024)
+    co.add_argument("--cmd-note", required=True)
+    co.add_argument("--last", type=int, default=3, help="launches averaged, the last of each run")
+    co.add_argument("--out-json", required=True)
+    co.add_argument("--out-txt", required=True)
     c = sp.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=5)
@@ -180,7 +409,8 @@ def main():
     r.add_argument("--out-json", required=True)
     r.add_argument("--out-txt", required=True)
     a = ap.parse_args()
-    {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic}[a.cmd_name](a)
+    {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "launch": cmd_launch,
+     "counters": cmd_counters}[a.cmd_name](a)
 
 
 if __name__ == "__main__":

@@ -2,22 +2,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
 
-One step = one pass over the hot path's two entry points: the causal MHA
-prefill at the Llama-2-7B attention shape (B=4, Hq=Hkv=32, S=2048, D=128,
-bf16) and the paged GQA decode (64 sequences, lengths U[512,4096], Hq=32,
-Hkv=8, D=128, 16-token blocks, row-major [block, head, slot, dim] pools; the
-MFMA-native pools are timed under "secondary").  Inputs are seeded synthetic
-tensors already resident in HBM.  W untimed warm-up steps, then exactly K
-timed steps bracketed by device synchronisations: the K decodes back to
-back, then the K prefills, with HIP events before, between and after them on
-the stream the kernels run on, which gives each kernel's mean launch
-duration without per-launch marker gaps.  Prints ONE JSON line.
+One step = one pass over the hot path's two entry points: the causal GQA
+prefill of the long-context workload (B=1, Hq=32, Hkv=8, S=8192, D=128,
+bf16; the largest dense prefill that the workloads name) and the paged GQA
+decode (64 sequences, lengths U[512,4096], Hq=32, Hkv=8, D=128, 16-token
+blocks, row-major [block, head, slot, dim] pools).  Inputs are seeded
+synthetic tensors already resident in HBM.  W untimed warm-up steps, then
+exactly K timed steps bracketed by device synchronisations: the K decodes
+back to back, then the K prefills, with HIP events before, between and
+after them on the stream the kernels run on, which gives each kernel's mean
+launch duration without per-launch marker gaps.  Prints ONE JSON line.
 
 `value` is the prefill throughput in TFLOP/s (algorithmic flops
-4*B*Hq*D*S(S+1)/2 over the prefill kernel's mean event time).  The decode
-K/V bandwidth, the long-context GQA prefill and the block-skip prefill are
-reported under "secondary".  The fp64 CPU oracle is timed on a bounded
-sample of the same prefill workload as "cpu_baseline".
+4*B*Hq*D*S(S+1)/2 over the prefill kernel's mean event time).  The MHA
+S=2048 prefill (the Llama-2-7B attention shape), the decode's K/V
+bandwidth and the other paths are reported under "secondary".  The fp64 CPU
+oracle is timed on a bounded sample of the same prefill workload as
+"cpu_baseline".  Counter figures (HBM bytes, MFMA-busy fraction, clock)
+come from profiles/counters.json and are reported only while the kernel
+source they were taken on is unchanged.
 """
 from __future__ import annotations
 
@@ -43,17 +46,23 @@ def kernel_hash(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    valid only while the kernel source is unchanged since the counters ran."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+def counters(workload: str):
+    """The committed rocprofv3 counter record of a workload (HBM bytes per
+    launch, MFMA-busy fraction, clock), or None if it is missing or the
+    kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(kernel)
+        rec = json.load(f).get(workload)
     if not rec or rec.get("source_sha256_16") != kernel_hash(rec["source"]):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def traffic_of(workload: str):
+    rec = counters(workload)
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def parse():
@@ -63,9 +72,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the GQA-8192 and block-skip measurements")
-    ap.add_argument("--cpu-heads", type=int, default=128,
-                    help="(batch, head) pairs of the prefill workload the CPU oracle runs")
+                    help="skip the measurements other than the step's two kernels")
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="query heads of the prefill workload the CPU oracle runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle sample until this much time has passed")
     return ap.parse_args()
@@ -91,10 +100,10 @@ def main():
     A.load()
 
     # ---------------------------------------------------------------- inputs
-    cp = CONFIGS["mha_causal_s2048"]
+    cp = CONFIGS["gqa_causal_s8192"]
     wp = prefill_inputs(cp["B"], cp["Hq"], cp["Hkv"], cp["S"], cp["D"], seed=cp["seed"])
-    # two copies of Q/K/V (2 x 192 MiB), used alternately, so that a launch
-    # cannot find its inputs in the 256 MB last-level cache
+    # two copies of Q/K/V (2 x 96 MiB), used alternately, so that a launch
+    # does not start with its inputs in the 256 MB last-level cache
     pre_in = [(wp.q.to(dev), wp.k.to(dev), wp.v.to(dev)) for _ in range(2)]
     o = torch.empty_like(pre_in[0][0])
     lse = torch.empty((cp["B"], cp["Hq"], cp["S"]), dtype=torch.float32, device=dev)
@@ -132,7 +141,7 @@ def main():
     # measurement of the decode kernel should not include.
     # The chip's clocks rise over roughly the first 10 ms of sustained load
     # (a prefill measured right after 1.5 ms of warm-up ran about 10% slower
-    # than after 30 ms), so the default warm-up is 50 steps (about 15 ms).
+    # than after 30 ms), so the default warm-up is 50 steps (about 30 ms).
     for i in range(args.warmup):
         run_prefill(i)
         run_decode(i)
@@ -163,7 +172,7 @@ def main():
             "kv_GBps": round(dec_gbps, 1), "frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(dec_s * 1e6, 2),
             "kv_bytes": kv_bytes, "launches": "decode_split + decode_merge",
-            "pool_layout": "rowmajor", "traffic": measured_traffic("decode_split"),
+            "pool_layout": "rowmajor", "traffic": traffic_of("paged_decode_gqa"),
         },
     }
 
@@ -208,7 +217,7 @@ def main():
             "kv_GBps": round(kv_bytes / mr / 1e9, 1),
             "frac_hbm_peak": round(kv_bytes / mr / 1e9 / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(mr * 1e6, 2), "launches": "decode_native + decode_merge",
-            "traffic": measured_traffic("decode_native")}
+            "traffic": traffic_of("paged_decode_gqa_mfma")}
         del rpools
 
         # the same cache with FP8 (E4M3) pools, one fp32 scale per pool: half
@@ -229,7 +238,7 @@ def main():
             "kv_GBps": round(fbytes / mf / 1e9, 1),
             "frac_hbm_peak": round(fbytes / mf / 1e9 / PEAK_HBM_GBPS, 4),
             "us_per_launch": round(mf * 1e6, 2), "kv_bytes": fbytes,
-            "speedup_vs_bf16_kv": round(dec_s / mf, 3),
+            "speedup_vs_bf16_kv": round(dec_s / mf, 3), "traffic": traffic_of("paged_decode_gqa_fp8"),
             "note": "E4M3 codes, one fp32 scale per pool; same q, table and lengths"}
         del fpools
 
@@ -299,6 +308,8 @@ def main():
                 "speedup_vs_dense": round(md / mk, 3),
                 "logical_kv_GBps": round(kvb / mk / 1e9, 1),
                 "read_kv_GBps": round(kvb * (1 - 0.5 * frac) / mk / 1e9, 1)}
+            if amp:
+                secondary[label]["traffic"] = traffic_of("paged_decode_blockskip_stress")
             del bpools
 
         # chunked prefill over the paged cache: 8 sequences with 3584 cached
@@ -317,20 +328,29 @@ def main():
         secondary["chunked_prefill_paged"] = {
             "TFLOPs": round(fc / mc / 1e12, 1), "frac_mfma_peak": round(fc / mc / 1e12 / PEAK_BF16_TFLOPS, 4),
             "us_per_launch": round(mc * 1e6, 1), "flops": fc,
+            "counters": counters("chunked_prefill_paged"),
             "note": "8 seqs x (3584 cached + 512 new) tokens, Hq=32 Hkv=8 D=128, bottom-right causal"}
         del ckp, cvp
 
-        c3 = CONFIGS["gqa_causal_s8192"]
-        w3 = prefill_inputs(c3["B"], c3["Hq"], c3["Hkv"], c3["S"], c3["D"], seed=c3["seed"])
-        q3, k3, v3 = w3.q.to(dev), w3.k.to(dev), w3.v.to(dev)
-        o3 = torch.empty_like(q3)
-        l3 = torch.empty((1, c3["Hq"], c3["S"]), dtype=torch.float32, device=dev)
-        m3 = time_it(lambda: A.attn_prefill(q3, k3, v3, o3, l3, True, w3.scale), 10)
-        f3 = prefill_flops(1, c3["Hq"], c3["S"], c3["D"], True)
-        secondary["gqa_causal_s8192"] = {
-            "TFLOPs": round(f3 / m3 / 1e12, 1), "frac_mfma_peak": round(f3 / m3 / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "us_per_launch": round(m3 * 1e6, 1)}
-        del q3, k3, v3, o3, l3
+        # the MHA prefill at the Llama-2-7B attention shape (two rotating copies)
+        c2 = CONFIGS["mha_causal_s2048"]
+        w2 = prefill_inputs(c2["B"], c2["Hq"], c2["Hkv"], c2["S"], c2["D"], seed=c2["seed"])
+        in2 = [(w2.q.to(dev), w2.k.to(dev), w2.v.to(dev)) for _ in range(2)]
+        o2 = torch.empty_like(in2[0][0])
+        l2 = torch.empty((c2["B"], c2["Hq"], c2["S"]), dtype=torch.float32, device=dev)
+        c2ctr = [0]
+
+        def run_c2():
+            q2, k2, v2 = in2[c2ctr[0] % 2]
+            c2ctr[0] += 1
+            A.attn_prefill(q2, k2, v2, o2, l2, True, w2.scale)
+        m2 = time_it(run_c2, 20)
+        f2 = prefill_flops(c2["B"], c2["Hq"], c2["S"], c2["D"], True)
+        secondary["mha_causal_s2048"] = {
+            "TFLOPs": round(f2 / m2 / 1e12, 1), "frac_mfma_peak": round(f2 / m2 / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "us_per_launch": round(m2 * 1e6, 1), "counters": counters("mha_causal_s2048"),
+            "note": "B=4 Hq=Hkv=32 S=2048 D=128 causal (Llama-2-7B attention shape)"}
+        del in2, o2, l2
 
         c5 = CONFIGS["blockskip_s32768"]
         for label, amp, boosted in (("blockskip_s32768", c5["amplitude"], c5["boosted"]),
@@ -361,7 +381,9 @@ def main():
                 "executed_TFLOPs": round(f5_exec / m5 / 1e12, 1),
                 "ms_per_launch": round(m5 * 1e3, 3),
                 "dense_kernel_ms": round(md * 1e3, 3),
-                "speedup_vs_dense": round(md / m5, 3)}
+                "speedup_vs_dense": round(md / m5, 3),
+                "counters": counters("blockskip_s32768" if amp == c5["amplitude"]
+                                     else "blockskip_s32768_stress")}
             del q5, k5, v5, o5, l5
 
     # ------------------------------------------------------------ CPU oracle
@@ -369,10 +391,11 @@ def main():
     if not args.no_cpu:
         from oracle import ref_prefill
         from workloads import upcast_f64
-        nh = max(1, min(args.cpu_heads, cp["B"] * cp["Hq"]))
+        nh = max(1, min(args.cpu_heads, cp["Hq"]))
+        nkv = max(1, nh // (cp["Hq"] // cp["Hkv"]))
         qs = upcast_f64(wp.q[:1, :nh])
-        ks = upcast_f64(wp.k[:1, :nh])
-        vs = upcast_f64(wp.v[:1, :nh])
+        ks = upcast_f64(wp.k[:1, :nkv])
+        vs = upcast_f64(wp.v[:1, :nkv])
         # repeat the sample until about --cpu-seconds of CPU work has been timed
         reps, t1 = 0, time.perf_counter()
         while True:
@@ -382,18 +405,21 @@ def main():
             if tc >= args.cpu_seconds:
                 break
         fl = prefill_flops(1, nh, cp["S"], cp["D"], True) * reps
+        cores, blas = os.cpu_count(), "unknown"
         try:
             from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+            info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+            if info:
+                cores = max(i.get("num_threads", 1) for i in info)
+                blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info}))
         except Exception:
-            cores = os.cpu_count()
+            pass
         cpu = {"value": round(fl / tc / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-               "kind": "oracle",
-               "sample": f"fp64 numpy oracle, {nh} of {cp['B'] * cp['Hq']} (batch, head) pairs of "
-                         f"the S=2048 D=128 causal prefill, all rows, run {reps} times; "
-                         f"{tc:.2f} s"}
+               "kind": "oracle", "blas": blas,
+               "sample": f"fp64 numpy oracle, {nh} of {cp['Hq']} query heads of the B=1 S=8192 "
+                         f"D=128 causal GQA prefill, all rows, run {reps} times; {tc:.2f} s"}
 
-    traffic = measured_traffic("prefill_bf16")
+    cnt = counters("gqa_causal_s8192")
     out = {
         "metric": "prefill attention TFLOP/s (% bf16 MFMA peak); paged decode KV GB/s (% HBM)",
         "value": round(pre_tflops, 2),
@@ -408,13 +434,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V; seeded paged pool)",
-        "config": {"workload": "mha_causal_s2048 prefill (B=4 Hq=Hkv=32 S=2048 D=128 causal) "
+        "config": {"workload": "gqa_causal_s8192 prefill (B=1 Hq=32 Hkv=8 S=8192 D=128 causal) "
                                "+ paged_decode_gqa (N=64 L~U[512,4096] Hq=32 Hkv=8 D=128 bs=16)",
                    "global_batch": cp["B"], "seq_len": cp["S"], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "prefill_bf16_kernel<128,causal>",
+                     "traffic": cnt.get("bytes_per_launch") if cnt else None,
+                     "mfma_busy_counter": cnt.get("mfma_busy_frac") if cnt else None,
+                     "clock_ghz_counter": cnt.get("clock_ghz") if cnt else None,
+                     "kernel": "prefill_bf16_kernel<128,causal>",
                      "us_per_launch": round(pre_s * 1e6, 2), "flops_per_launch": p_flops,
                      "timing": f"HIP events around {args.steps} back-to-back launches"},
         "cpu_baseline": cpu,
