@@ -278,7 +278,7 @@ def attn_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, block_si
 def attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size: int, o,
                                 lse, scale: float, lam: float, workspace, skip_bitmap=None,
                                 skipped_blocks=None, stream=None, layout: str = "mfma") -> None:
-    """Paged decode with block skipping (MFMA-native pools); skip_bitmap is
+    """Paged decode with block skipping (either pool layout); skip_bitmap is
     uint8 [N, Hkv, max_blocks] or None, skipped_blocks one 64-bit device
     integer (incremented) or None."""
     N, Hq, Hkv, D, NB, nbytes = _decode_check(q, k_pool, v_pool, block_table, seq_lens,
@@ -417,9 +417,10 @@ def decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, block_size: i
 
 
 def decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, lam: float,
-                           block_size: int = 16, scale: Optional[float] = None, workspace=None):
+                           block_size: int = 16, scale: Optional[float] = None, workspace=None,
+                           layout: str = "mfma"):
     """Allocate O, LSE, the skip bitmap and counter (and the workspace unless
-    given) and run the block-skip paged decode on MFMA-native pools.
+    given) and run the block-skip paged decode on pools in ``layout``.
     Returns (o, lse, skip_bitmap, skipped_blocks)."""
     N, Hq, D = q.shape
     Hkv = k_pool.shape[1]
@@ -433,7 +434,7 @@ def decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, lam: float,
         nbytes = attn_decode_workspace_bytes(N, Hq, D, int(block_table.shape[1]), block_size)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     attn_decode_paged_blockskip(q, k_pool, v_pool, block_table, seq_lens, block_size, o, lse,
-                                scale, lam, workspace, bm, cnt, layout="mfma")
+                                scale, lam, workspace, bm, cnt, layout=layout)
     return o, lse, bm, cnt
 
 

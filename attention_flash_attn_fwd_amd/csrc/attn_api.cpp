@@ -135,7 +135,6 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool,
   if (!finite_pos(scale)) return ATTN_ERR_INVALID_ARG;
   if (kv_layout != ATTN_KV_ROWMAJOR && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_INVALID_ARG;
   if (skip && !(lambda > 0.f && lambda < 1.f)) return ATTN_ERR_INVALID_ARG;
-  if (skip && kv_layout != ATTN_KV_MFMA) return ATTN_ERR_UNSUPPORTED;
   if (fp8 && (!finite_pos(k_scale) || !finite_pos(v_scale))) return ATTN_ERR_INVALID_ARG;
   if (block_size != 16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;

@@ -127,6 +127,20 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most n (wave-uniform, 0..15) vector-memory operations of
+// this wave are in flight; a larger n waits for all of them.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+#define ATTN_WAIT_CASE(k) \
+  case k: wait_vmem<k>(); break;
+    ATTN_WAIT_CASE(1) ATTN_WAIT_CASE(2) ATTN_WAIT_CASE(3) ATTN_WAIT_CASE(4) ATTN_WAIT_CASE(5)
+    ATTN_WAIT_CASE(6) ATTN_WAIT_CASE(7) ATTN_WAIT_CASE(8) ATTN_WAIT_CASE(9) ATTN_WAIT_CASE(10)
+    ATTN_WAIT_CASE(11) ATTN_WAIT_CASE(12) ATTN_WAIT_CASE(13) ATTN_WAIT_CASE(14) ATTN_WAIT_CASE(15)
+#undef ATTN_WAIT_CASE
+    default: wait_vmem<0>(); break;
+  }
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -901,6 +915,222 @@ __global__ __launch_bounds__(64, kDecodeWavesPerSimd) void decode_skip_kernel(De
   }
 }
 
+// The same block skip on row-major pools ([block, head, slot, dim]), so one
+// cache layout serves the dense decode, the block-skip decode and the
+// chunked prefill.  K comes straight into operand registers (lane (h, g4)
+// reads 16 bytes of token h's row per 32-dim step); a kept block's V rows
+// are copied into an LDS stage (asynchronous 16-byte-per-lane copy, chunks
+// XOR-permuted as in the split kernel) and read back transposed.  The order
+// of one step is that of the MFMA-native kernel: score and decide block j+1,
+// copy its V if kept, load the K of block j+3, then finish block j once its
+// V copy (issued one step earlier) has landed.
+template <int D>
+__global__ __launch_bounds__(64, kDecodeWavesPerSimd) void decode_skip_rm_kernel(DecParams p) {
+  using T = DTile<D>;
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int RB = D * 2;               // bytes of one token row
+  constexpr int RUN = kBlk * RB;          // bytes of one (block, head)
+  constexpr int NVI = RUN / 1024;         // copy instructions per V block
+  constexpr int RPI = 1024 / RB;          // rows per copy instruction
+  __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[2 * RUN];
+  LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+
+  const int kvh = blockIdx.x, split = blockIdx.y, n = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int h = lane & 15, g4 = lane >> 4;
+  const int L = p.seq_lens[n];
+  const int tok_begin = split * kDecodeSplitTokens;
+  if (L <= 0 || tok_begin >= L) return;
+  const int n_tok = min(L - tok_begin, kDecodeSplitTokens);
+  const int G = p.G;
+
+  const int32_t* trow = p.table + (size_t)n * p.max_blocks;
+  const int lb0 = tok_begin / kBlk;
+  const int n_blk = (n_tok + kBlk - 1) / kBlk;
+  const bool in_table = lb0 + n_blk <= p.max_blocks;
+  int my_ph = 0;
+  if (in_table && lane < n_blk) my_ph = trow[lb0 + lane];
+  bf16x8 qB[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (h < G)
+      qB[ks] = *reinterpret_cast<const bf16x8*>(p.q + ((size_t)n * p.Hq + kvh * G + h) * D +
+                                                ks * 32 + g4 * 8);
+    else
+      qB[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), visible to the compiler
+  const bool lane_ok = lane >= n_blk || (my_ph >= 0 && my_ph < p.num_blocks);
+  const bool bad = !in_table || !__all(lane_ok);
+  const size_t slot = ((size_t)n * p.Hq + kvh * G + h) * p.n_split + split;
+  if (bad) {
+    if (h < G) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = f32x4{NAN, NAN, NAN, NAN};
+      if (g4 == 0) p.ws_lse[slot] = NAN;
+    }
+    return;
+  }
+
+  const size_t blk_stride = (size_t)p.Hkv * RUN;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k_pool) + (size_t)kvh * RUN;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v_pool) + (size_t)kvh * RUN;
+  const uint32_t k_off = (uint32_t)(h * RB + g4 * 16);  // + ks * 64
+  auto load_k = [&](int j, bf16x8* kb) {
+    const size_t ph = (size_t)__builtin_amdgcn_readlane(my_ph, j);
+    const unsigned char* src = kbase + ph * blk_stride + k_off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kb[ks] = __builtin_bit_cast(
+          bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ks * 64)));
+  };
+  // V rows of block j into LDS stage j % 2; rows past the sequence end
+  // re-read its last token, so every row holds finite data
+  auto copy_v = [&](int j) {
+    const int ph = __builtin_amdgcn_readlane(my_ph, j);
+    const int valid = min(kBlk, n_tok - j * kBlk);
+    const uint32_t st = smem_base + (j & 1) * RUN;
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) {
+      const int row = i * RPI + (lane * 16) / RB;
+      const int slotc = ((lane * 16) % RB) / 16;
+      const uint32_t vo = (uint32_t)min(row, valid - 1) * RB + ((slotc ^ T::swz_v(row)) << 4);
+      dma16(vbase + (size_t)ph * blk_stride, vo, st + i * 1024);
+    }
+  };
+
+  const float sl2 = p.sl2;
+  auto scores = [&](int j, const bf16x8* kb) -> f32x4 {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qB[ks], s, 0, 0, 0);
+    // branch-free tail mask (see decode_skip_kernel)
+    const int valid = n_tok - j * kBlk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = 4 * g4 + i < valid ? s[i] : -INFINITY;
+    return s;
+  };
+  auto block_max = [&](const f32x4& s) -> float {
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    return half_swap_max(mx) * sl2;
+  };
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_used = kUnset, l = 0.f;
+  float m_true = kUnset;  // running max of the split's earlier blocks (log2 units)
+  unsigned skipped = 0;
+  auto decide = [&](int j, float tmx) -> bool {
+    bool neg = true;  // padding columns (h >= G) never keep a block
+    if (h < G) neg = m_true > 0.5f * kUnset && tmx - m_true < p.thr;
+    const bool sk = j > 0 && __all(neg);
+    m_true = fmaxf(m_true, tmx);
+    if (lane == 0 && p.skip_map)
+      p.skip_map[((size_t)n * p.Hkv + kvh) * p.max_blocks + lb0 + j] = sk ? 1 : 0;
+    skipped += sk ? 1u : 0u;
+    return sk;
+  };
+  // V^T fragment of dims db*16 + lane%16, tokens 4*g4 .. +3: transposing
+  // read of rows 4*g4 + (lane%16)/4, dims db*16 + 4*(lane%4) .. +3
+  const int vs = lane & 15;
+  const int v_row = 4 * g4 + (vs >> 2);
+  auto finish = [&](int j, f32x4 s, float tmx) {
+    const LDS_AS unsigned char* vl = smem + (j & 1) * RUN;
+    if (__any(tmx > m_used + 8.f)) {
+      const float m_new = fmaxf(m_used, tmx);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float nm = -m_used;
+    const uint32_t pk0 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[0], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[1], sl2, nm)));
+    const uint32_t pk1 = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[2], sl2, nm)),
+                                   __builtin_amdgcn_exp2f(fmaf(s[3], sl2, nm)));
+    l += __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk0), kOnes2, 0.f, false) +
+         __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk1), kOnes2, 0.f, false);
+    const u32x2 pw = {pk0, pk1};
+    const s16x4 pB = __builtin_bit_cast(s16x4, pw);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + 4 * (vs & 3);
+      const int c = d >> 3;
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(vl + v_row * RB + ((c ^ T::swz_v(v_row)) << 4) + (d & 7) * 2));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pB, acc[db], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage read before it is refilled
+  };
+
+  bf16x8 k0[NKS], k1[NKS], k2[NKS];
+  f32x4 s_cur;
+  float t_cur;
+  bool keep_cur;
+  // step j: score and decide block j+1 (its K has arrived), copy its V if
+  // kept and load the K of block j+3 into the buffer block j used; then
+  // finish block j once the V copy issued one step earlier has landed (the
+  // operations issued after it are counted: those copies and loads)
+  auto step = [&](int j, const bf16x8* ksc, bf16x8* kld) {
+    f32x4 s_n = {0.f, 0.f, 0.f, 0.f};
+    float t_n = 0.f;
+    bool keep_n = false;
+    int later = j + 2 < n_blk ? NKS : 0;  // K of block j+2, loaded last step
+    if (j + 1 < n_blk) {
+      s_n = scores(j + 1, ksc);
+      t_n = block_max(s_n);
+      keep_n = !decide(j + 1, t_n);
+      if (keep_n) {
+        copy_v(j + 1);
+        later += NVI;
+      }
+      if (j + 3 < n_blk) {
+        load_k(j + 3, kld);
+        later += NKS;
+      }
+    }
+    if (keep_cur) {
+      wait_vmem_upto(later);
+      finish(j, s_cur, t_cur);
+    }
+    s_cur = s_n;
+    t_cur = t_n;
+    keep_cur = keep_n;
+  };
+  load_k(0, k0);
+  if (n_blk > 1) load_k(1, k1);
+  s_cur = scores(0, k0);
+  t_cur = block_max(s_cur);
+  keep_cur = !decide(0, t_cur);
+  copy_v(0);
+  if (n_blk > 2) load_k(2, k2);
+  for (int j = 0; j < n_blk; j += 3) {
+    step(j, k1, k0);
+    if (j + 1 >= n_blk) break;
+    step(j + 1, k2, k1);
+    if (j + 2 >= n_blk) break;
+    step(j + 2, k0, k2);
+  }
+
+  if (lane == 0 && skipped && p.skip_count)
+    atomicAdd(p.skip_count, (unsigned long long)skipped);
+  float lt = l + __shfl_xor(l, 16);
+  lt = half_swap_add(lt);
+  if (h < G) {
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(p.ws_o + slot * D + db * 16 + 4 * g4) = acc[db] * inv;
+    if (g4 == 0) p.ws_lse[slot] = m_used + __log2f(lt);
+  }
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
@@ -1003,8 +1233,10 @@ hipError_t launch_d(const DecParams& p, int N, int layout, bool skip, bool fp8,
                     hipStream_t stream) {
   if (fp8)
     hipLaunchKernelGGL((decode_fp8_kernel<D, 2>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
-  else if (skip)
+  else if (skip && layout == 1)
     hipLaunchKernelGGL((decode_skip_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
+  else if (skip)
+    hipLaunchKernelGGL((decode_skip_rm_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
   else if (layout == 1)
     hipLaunchKernelGGL((decode_native_kernel<D>), dim3(p.Hkv, p.n_split, N), dim3(64), 0, stream, p);
   else
@@ -1041,7 +1273,6 @@ hipError_t launch_decode_paged(const DecodeArgs& a, hipStream_t stream) {
   p.skip_map = a.skip_bitmap;
   p.skip_count = a.skip_count;
   if (p.G > 16) return hipErrorInvalidValue;
-  if (a.skip && a.layout != 1) return hipErrorInvalidValue;
   if (a.fp8 && a.skip) return hipErrorInvalidValue;
   const bool sk = a.skip != 0, f8 = a.fp8 != 0;
   return a.D == 64 ? launch_d<64>(p, a.N, a.layout, sk, f8, stream)

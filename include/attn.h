@@ -225,9 +225,8 @@ int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_p
 /* Paged decode with block skipping ("高效部署稀疏注意力加速方案：BLASST方法详解与
  * 实践指南", 架构与组件: a running maximum from the blockwise online softmax and
  * a threshold lambda decide which blocks matter; the others lose their exp,
- * their V load and their matrix product).  Arguments as attn_decode_paged,
- * plus:
- *   kv_layout     : must be ATTN_KV_MFMA (ATTN_ERR_UNSUPPORTED otherwise)
+ * their V load and their matrix product).  Arguments as attn_decode_paged
+ * (either pool layout), plus:
  *   lambda        : threshold, 0 < lambda < 1
  *   skip_bitmap   : uint8 [N, Hkv, max_blocks_per_seq] or NULL; entry
  *                   (n, g, j) is set to 1 if logical block j of sequence n

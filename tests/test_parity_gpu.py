@@ -349,7 +349,8 @@ SPLIT = 512  # tokens per split of the split-KV decode
 def _run_decode_skip(d, lam):
     q, kp, vp = d.q.cuda(), d.k_pool.cuda(), d.v_pool.cuda()
     o, lse, bm, cnt = A.decode_paged_blockskip(q, kp, vp, d.block_table.cuda(),
-                                               d.seq_lens.cuda(), lam, scale=d.scale)
+                                               d.seq_lens.cuda(), lam, scale=d.scale,
+                                               layout=d.layout)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.cpu().numpy(), bm.cpu().numpy(), int(cnt.item())
 
@@ -371,16 +372,18 @@ def _check_decode_skip(d, lam, what, min_frac=0.0):
     return o, lse
 
 
-def test_decode_blockskip_stress_decisions():
-    say("decode block skip: sink stress input, lambda 1e-3")
-    d = decode_inputs(16, 32, 8, 128, seed=97, lmin=100, lmax=3000, tail="nan", layout="mfma",
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_decode_blockskip_stress_decisions(layout):
+    say(f"decode block skip: sink stress input, lambda 1e-3 ({layout} pools)")
+    d = decode_inputs(16, 32, 8, 128, seed=97, lmin=100, lmax=3000, tail="nan", layout=layout,
                       sink_amplitude=12.0, sink_frac=1 / 64)
-    _check_decode_skip(d, 1e-3, "decode skip stress", min_frac=0.2)
+    _check_decode_skip(d, 1e-3, f"decode skip stress ({layout})", min_frac=0.2)
 
 
-def test_decode_blockskip_tiny_lambda_matches_dense():
-    say("decode block skip with lambda=1e-30: nothing skipped, equals the dense decode")
-    d = decode_inputs(8, 32, 8, 128, seed=98, lmin=1, lmax=2000, tail="nan", layout="mfma")
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_decode_blockskip_tiny_lambda_matches_dense(layout):
+    say(f"decode block skip with lambda=1e-30: nothing skipped, equals the dense decode ({layout})")
+    d = decode_inputs(8, 32, 8, 128, seed=98, lmin=1, lmax=2000, tail="nan", layout=layout)
     o, lse, bm, cnt = _run_decode_skip(d, 1e-30)
     assert cnt == 0 and bm.sum() == 0
     od, ld = _run_decode(d)
@@ -388,10 +391,11 @@ def test_decode_blockskip_tiny_lambda_matches_dense():
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 1, 64), (8, 8, 128), (32, 2, 128)])
-def test_decode_blockskip_edge_lengths(Hq, Hkv, D):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_decode_blockskip_edge_lengths(Hq, Hkv, D, layout):
     lens = [1, 16, 17, 511, 512, 513, 1000, 0, 1024, 1537]
-    say(f"decode block skip edge lengths Hq{Hq} Hkv{Hkv} D{D}")
-    d = decode_inputs(len(lens), Hq, Hkv, D, seed=99 + D, lens=lens, tail="nan", layout="mfma",
+    say(f"decode block skip edge lengths Hq{Hq} Hkv{Hkv} D{D} ({layout})")
+    d = decode_inputs(len(lens), Hq, Hkv, D, seed=99 + D, lens=lens, tail="nan", layout=layout,
                       sink_amplitude=12.0, sink_frac=1 / 32)
     o, lse, bm, cnt = _run_decode_skip(d, 1e-3)
     z = lens.index(0)
@@ -400,6 +404,28 @@ def test_decode_blockskip_edge_lengths(Hq, Hkv, D):
     dk = dataclasses.replace(d, q=d.q[keep], block_table=d.block_table[keep],
                              seq_lens=d.seq_lens[keep], N=len(keep))
     _check_decode_skip(dk, 1e-3, f"decode skip edges Hq{Hq} Hkv{Hkv} D{D}")
+
+
+def test_one_rowmajor_cache_serves_prefill_decode_and_skip():
+    """One row-major paged cache serves every paged path: the chunked prefill
+    with one query per sequence (the query at position L-1 sees all L keys),
+    the dense decode and the block-skip decode with a lambda that skips
+    nothing give the same rows, and match the oracle."""
+    say("one row-major cache: chunked prefill (1 query), dense decode, block-skip decode")
+    d = decode_inputs(12, 32, 8, 128, seed=141, lmin=1, lmax=1500, tail="nan", layout="rowmajor")
+    od, ld = _run_decode(d)
+    os_, ls, bm, cnt = _run_decode_skip(d, 1e-30)
+    assert cnt == 0
+    N = d.N
+    cu = torch.arange(N + 1, dtype=torch.int32)
+    op, lp = A.prefill_paged(d.q.cuda(), cu.cuda(), d.k_pool.cuda(), d.v_pool.cuda(),
+                             d.block_table.cuda(), d.seq_lens.cuda(), 1, scale=d.scale)
+    torch.cuda.synchronize()
+    op, lp = op.float().cpu().numpy(), lp.cpu().numpy()
+    ro, rl = _ref_decode(d)
+    _compare(od, ld, ro, rl, TOL["bf16"], "one cache: decode")
+    _compare(os_, ls, ro, rl, TOL["bf16"], "one cache: block-skip decode")
+    _compare(op, lp, ro, rl, TOL["bf16"], "one cache: chunked prefill")
 
 
 # ---------------------------------------------------------------- block skip
