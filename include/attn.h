@@ -69,7 +69,8 @@ typedef enum {
  * process ends). */
 #define ATTN_DECODE_STATIC_SCRATCH_BYTES (16u << 20)
 
-/* Static, human-readable text for a status code (never NULL). */
+/* Static, human-readable text for a status code (never NULL).  Plumbing of
+ * this interface: no passage of the source pages defines it. */
 const char* attn_status_string(int status);
 
 /* 1 if a device whose gcnArchName is `gcn_arch_name` (e.g. "gfx950" or
@@ -107,7 +108,9 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * attn_prefill_f32 - as attn_prefill with float32 Q, K, V and O and true fp32
- * products and sums throughout (no bf16/tf32 rounding anywhere).
+ * products and sums throughout (no bf16/tf32 rounding anywhere).  The same
+ * operation as attn_prefill (same passage); the pages name no number type,
+ * and this entry point serves the fp32 workload.
  */
 int attn_prefill_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int B, int Hq, int Hkv, int S, int D, int causal, float scale,
@@ -149,7 +152,8 @@ int attn_prefill_blockskip(const void* q, const void* k, const void* v, void* o,
 /*
  * attn_decode_workspace_bytes - device workspace attn_decode_paged needs for
  * the given sizes (0 for invalid sizes).  Holds one partial output and one
- * partial log-sum-exp per (sequence, query head, KV split).
+ * partial log-sum-exp per (sequence, query head, KV split).  Plumbing of the
+ * split-KV decode: no passage of the source pages defines it.
  */
 size_t attn_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_blocks_per_seq,
                                    int block_size);
