@@ -173,13 +173,15 @@ struct Tile {
   static constexpr int STAGE = KT + VT;
   static constexpr int NST = 4;               // LDS stages: t-1 (role B), t, t+1, t+2 in flight
   static constexpr size_t lds_bytes = (size_t)NST * STAGE;
-  // Block skip: K and V in rings of their own, K tile t in K stage t % 4 and
-  // V tile t in V stage t % 3 (a V tile is only copied once it is known to
-  // be needed, see the block-skip loop).
+  // Block skip: K and V in rings of their own, V tile t in V stage t % 4 at
+  // the start of LDS (so that every V operand read is a lane base plus an
+  // immediate offset), then K tile t in K stage t % 4; the same bytes as the
+  // dense layout.  A V tile is only copied once it is known to be needed
+  // (see the block-skip loop).
+  static constexpr uint32_t VRING = 0, KRING = NST * VT;
   static constexpr int VPW = VSL / 4;         // V copy blocks per wave of the copying group
   static_assert(VSL % 4 == 0, "a V tile splits evenly over four waves");
-  static constexpr int VST = 3;
-  static constexpr size_t skip_lds_bytes = (size_t)NST * KT + VST * VT;
+  static constexpr int KPW = (KSL + 3) / 4;   // K copy blocks per wave of group 1 (see issue_k)
 };
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -210,8 +212,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   LDS_AS unsigned char* smem = (LDS_AS unsigned char*)smem_raw;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-  __shared__ __attribute__((aligned(16))) int vote_lds[2][kWaves];  // block skip: (tile << 1) | negligible
-  __shared__ unsigned char skip_lds[kWaves][256];  // block skip: decisions, 256 tiles a row
+  // block skip: the votes, (tile << 1) | negligible, for even and odd tiles,
+  // then a landing area for the lanes of a vote write that carry no vote
+  __shared__ __attribute__((aligned(16))) int vote_lds[3 * kWaves + 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,10 +313,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // LDS byte offsets of K tile t and V tile t (dense: one ring of K+V
     // stages continuing across items; block skip: separate K and V rings)
     auto k_stage = [&](int t) -> uint32_t {
-      return SKIP ? (uint32_t)(t & 3) * T::KT : (uint32_t)((t + ring) % T::NST) * T::STAGE;
+      return SKIP ? T::KRING + (uint32_t)(t & 3) * T::KT : (uint32_t)((t + ring) % T::NST) * T::STAGE;
     };
     auto v_stage = [&](int t) -> uint32_t {
-      return SKIP ? (uint32_t)(T::NST * T::KT + (t % T::VST) * T::VT)
+      return SKIP ? T::VRING + (uint32_t)(t & 3) * T::VT
                   : (uint32_t)((t + ring) % T::NST) * T::STAGE + T::KT;
     };
 
@@ -443,11 +446,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // Block skip: K and V tiles are copied separately, each by one wave
     // group and dealt round robin to its four waves: group 1 copies every K
     // tile (tile j+3 in its VALU phase j), the group that copies a V tile is
-    // chosen by the decisions (see vote_collect).  Slot g of a block is row
-    // g / SL, chunk g % SL, as above; keys past the end are clamped to the
-    // last key.
-    constexpr int KB_HI = (T::KSL + 3) / 4, KB_LO = T::KSL / 4;
-    const bool kb_hi = (wave & 3) < T::KSL % 4;
+    // chosen by the decisions (see vote_collect).  Every group-1 wave issues
+    // KPW blocks of a K tile: a wave with one block fewer copies its last
+    // block twice (the same bytes to the same place), so that its count of
+    // copies in flight, and with it the wait at the end of a phase, is fixed.
+    // Slot g of a block is row g / SL, chunk g % SL, as above; keys past the
+    // end are clamped to the last key.
+    const int kq = wave & 3;
+    const int kb_last = kq + 4 * (T::KPW - 1) < T::KSL ? kq + 4 * (T::KPW - 1) : kq + 4 * (T::KPW - 2);
+    auto kblk = [&](int j) { return j == T::KPW - 1 ? kb_last : kq + 4 * j; };
     auto slot_off = [&](int g, int sl) -> uint32_t {
       const int r = g / sl, c = g % sl;
       return (uint32_t)r * T::RB + (c < T::CH ? c : 0) * 16;
@@ -455,12 +462,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // a wave's own copy offsets: K blocks in group 1, V blocks in group 0
     // (group 1 copies a V tile only when group 0 does not need it, and then
     // forms the offsets as it goes)
-    constexpr int NOFF = KB_HI > T::VPW ? KB_HI : T::VPW;
+    constexpr int NOFF = T::KPW > T::VPW ? T::KPW : T::VPW;
     uint32_t coff[SKIP ? NOFF : 1];
     if constexpr (SKIP) {
 #pragma unroll
       for (int j = 0; j < NOFF; ++j)
-        coff[j] = slot_off(((wave & 3) + 4 * j) * 64 + lane, grp == 1 ? T::KSL : T::VSL);
+        coff[j] = grp == 1 ? slot_off(kblk(j < T::KPW ? j : 0) * 64 + lane, T::KSL)
+                           : slot_off((kq + 4 * j) * 64 + lane, T::VSL);
     }
     // offset of slot g of a block array with sl slots per row, with rows past
     // lim clamped to row lim
@@ -469,21 +477,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       return o - (uint32_t)(r - min(r, lim)) * T::RB;
     };
     // (whole: the caller knows that tile t has all BN keys)
-    auto issue_k = [&](int t, bool whole) {  // a group-1 wave's blocks of K tile t
+    auto issue_k = [&](int t, bool whole) {  // a group-1 wave's KPW blocks of K tile t
       const uint32_t st = smem_base + k_stage(t);
       const int key0 = t * BN;
       const uint16_t* src = Kg + (size_t)key0 * D;
       if (whole || key0 + BN <= S) {
 #pragma unroll
-        for (int j = 0; j < KB_HI; ++j) {
-          if (j == KB_LO && !kb_hi) break;
-          dma16(src, coff[j], st + ((wave & 3) + 4 * j) * 1024);
-        }
+        for (int j = 0; j < T::KPW; ++j) dma16(src, coff[j], st + kblk(j) * 1024);
       } else {
 #pragma unroll
-        for (int j = 0; j < KB_HI; ++j) {
-          if (j == KB_LO && !kb_hi) break;
-          const int i = (wave & 3) + 4 * j;
+        for (int j = 0; j < T::KPW; ++j) {
+          const int i = kblk(j);
           dma16(src, clamp_off(coff[j], i * 64 + lane, T::KSL, S - 1 - key0), st + i * 1024);
         }
       }
@@ -641,7 +645,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         pend = false;
       }
     };
-    auto softmax = [&](f32x16* sc, float tmx, uint32_t (*pk)[8]) {
+    // the lazy rescale for a tile whose scaled row max is tmx
+    auto rescale = [&](float tmx) {
       if (__any(tmx > m_used + 8.f)) {
         const float m_new = fmaxf(m_used, tmx);
         const float alpha = fast_exp2(m_used - m_new);
@@ -657,21 +662,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         }
         m_used = m_new;
       }
-      const float nm = -m_used;
+    };
+    // P = exp2(scores * sl2 + nm) rounded to bf16 (nm = -m_used); returns
+    // the row sum of the bf16-rounded P (the values P.V uses), two per dot2
+    auto exps = [&](f32x16* sc, uint32_t (*pk)[8], float nm) -> float {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2)
           pk[kb][i >> 1] = pack_bf16(fast_exp2(fmaf(sc[kb][i], sl2, nm)),
                                      fast_exp2(fmaf(sc[kb][i + 1], sl2, nm)));
-      // row sum of the bf16-rounded P (the values P.V uses), two per dot2
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[0][j]), kOnes2, rs0, false);
         rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[1][j]), kOnes2, rs1, false);
       }
-      l += rs0 + rs1;
+      return rs0 + rs1;
+    };
+    auto softmax = [&](f32x16* sc, float tmx, uint32_t (*pk)[8]) {
+      rescale(tmx);
+      l += exps(sc, pk, -m_used);
     };
     // O^T += V^T P^T for key tile t; V^T fragments come from the transposing
     // LDS read, running ahead of the MFMAs
@@ -708,81 +719,85 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     // negligible?), published in LDS.  The other waves of the wave group run
     // the same phase, so their votes on t arrive within a few instructions;
     // vote_collect waits for the group's four (the other wave of this
-    // wave's 64-row tile is among them).  The copy issue sits between
-    // publish and collect, hiding the LDS round trip.  V tile t is copied by
-    // group 0 if one of its 64-row tiles keeps t, else by group 1 if one of
-    // its tiles does (group 1 runs its phase after group 0's and sees group
-    // 0's votes); it is not copied at all when every tile of the workgroup
-    // skips t.  The wait is bounded: a wave whose group's votes do not all
-    // arrive keeps the tile (always exact), republishes its own vote as
-    // "keep" before the phase's closing barrier (so group 1 knows that group
-    // 0 needs the tile), and copies the whole V tile itself (lost = true).
-    // One wave of each 64-row tile records the decisions on its live tiles,
-    // first in an LDS row of 256 tiles, written to the bitmap when the row is
-    // full and at the end (a store per tile cost 8%).  vote_collect is true
-    // if tile t is skipped; copyv says whether this wave's group copies V
-    // tile t.
-    const bool records = SKIP && ((slot / p.gw) & 1) == 0;
-    auto vote_publish = [&](int t, float tmx_t, bool live) -> bool {
-      bool neg = true;
-      if (live)
-        neg = (tmx_t == -INFINITY) || (m_true > 0.5f * kUnset && tmx_t - m_true < thr) ||
-              (q0 + n >= S);
-      const bool all_neg = __all(neg);
-      if (lane == 0)
-        __hip_atomic_store(&vote_lds[t & 1][wave], (t << 1) | (all_neg ? 1 : 0), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    // wave's 64-row tile is among them).  Work that does not depend on the
+    // decision sits between publish and collect, hiding the LDS round trip.
+    // V tile t is copied by group 0 if one of its 64-row tiles keeps t, else
+    // by group 1 if one of its tiles does (group 1 runs its phase after group
+    // 0's and sees group 0's votes); it is not copied at all when every tile
+    // of the workgroup skips t.  The wait is bounded: a wave whose group's
+    // votes do not all arrive keeps the tile (always exact), republishes its
+    // own vote as "keep" before the phase's closing barrier (so group 1 knows
+    // that group 0 needs the tile), and copies the whole V tile itself (lost
+    // = true).  Votes on even and odd tiles use separate slots, so a slot is
+    // rewritten only after every wave has read it (two barriers later).
+    // Lane 0 writes the vote; the other lanes of the same write land in a
+    // scratch area, which spares switching lanes off and on.
+    // The decision values below are wave-uniform ints built from ballots
+    // (bit w of a ballot over lanes 0-7 = wave w), so that they stay in
+    // scalar registers.
+    LDS_AS int* const vote_w =
+        (LDS_AS int*)&vote_lds[0] + (lane == 0 ? wave : 2 * kWaves + lane - 1);
+    // lanes whose query row is past the end vote "negligible" on every tile
+    const uint64_t rows_out = __ballot(q0 + n >= S);
+    // 1 if every row of this wave is negligible on tile t
+    auto vote_publish = [&](int t, float tmx_t, bool live) -> int {
+      int all_neg = 1;
+      if (live) {
+        const bool neg = (tmx_t == -INFINITY) | ((m_true > 0.5f * kUnset) & (tmx_t - m_true < thr));
+        all_neg = (__ballot(neg) | rows_out) == ~0ull ? 1 : 0;
+      }
+      __hip_atomic_store(vote_w + (t & 1) * kWaves, (t << 1) | all_neg, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
       return all_neg;
     };
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
     // lanes 0-7 each read one wave's vote; ballots then test the tags and
-    // gather the verdicts (bit w = wave w)
-    const uint32_t vote_lane = lane < kWaves ? lane : 0;
-    const uint64_t grp_mask = grp == 0 ? 0x0Full : 0xFFull;  // group 1 also waits for group 0's votes
-    auto vote_collect = [&](int t, bool all_neg, bool& copyv, bool& lost) -> bool {
-      int v = 0;
-      bool got = false;
+    // gather the verdicts
+    const LDS_AS int* const vote_r = (const LDS_AS int*)&vote_lds[0] + (lane & (kWaves - 1));
+    const uint32_t wait_mask = grp == 0 ? 0x0Fu : 0xFFu;  // group 1 also waits for group 0's votes
+    // 1 if tile t is skipped; copyv = 1 if this wave's group copies V tile t
+    auto vote_collect = [&](int t, int all_neg, int& copyv, int& lost) -> int {
+      uint32_t keeps = 0, ready = 0;
       for (int spin = 0; spin < (1 << 16); ++spin) {
-        v = *(volatile LDS_AS int*)(&vote_lds[t & 1][vote_lane]);
-        if ((__ballot((v >> 1) == t) & grp_mask) == grp_mask) { got = true; break; }
+        const int d = *(volatile const LDS_AS int*)(vote_r + (t & 1) * kWaves) ^ (t << 1);
+        keeps = (uint32_t)__ballot(d == 0) & 0xFFu;  // waves with a row that keeps t
+        ready = (uint32_t)__ballot((unsigned)d <= 1u) & wait_mask;
+        if (ready == wait_mask) break;
       }
-      lost = !got;
-      const uint64_t keeps = __ballot(!(v & 1));   // waves with a row that keeps t
-      const bool need0 = (keeps & 0x0Full) != 0, need1 = (keeps & 0xF0ull) != 0;
+      lost = ready != wait_mask ? 1 : 0;
       // does a 64-row tile of group 0 keep t?  then group 0 copies V tile t;
       // else group 1 does if one of its tiles keeps it
-      copyv = grp == 0 ? need0 : (need1 && !need0);
-      const bool other_neg = ((keeps >> pwave) & 1) == 0;
+      const int need0 = (keeps & 0x0Fu) != 0 ? 1 : 0, need1 = (keeps & 0xF0u) != 0 ? 1 : 0;
+      copyv = grp == 0 ? need0 : need1 & (need0 ^ 1);
+      const int other_neg = ((keeps >> pwave) & 1u) ^ 1u;
       if (__builtin_expect(lost, 0)) {
         // the wait ran out: keep the tile, say so, and copy V tile t
-        copyv = true;
-        if (lane == 0)
-          __hip_atomic_store(&vote_lds[t & 1][wave], t << 1, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
+        copyv = 1;
+        __hip_atomic_store(vote_w + (t & 1) * kWaves, t << 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        return 0;
       }
-      const bool sk = got && all_neg && other_neg;
-      if (records && t < wave_tiles) {
-        if (lane == 0) skip_lds[wave][t & 255] = sk ? 1 : 0;
-        skipped += sk ? 1u : 0u;
-      }
-      return sk;
+      return all_neg & other_neg;
     };
-    // A recording wave's decisions on tiles t0 .. t0+255 from its LDS row to
-    // the bitmap, a byte per lane and store.  The buffer resource ends at the
-    // wave's last live tile, so the range check drops the rest and exactly
-    // four stores are issued, which the copy wait of the phase counts.
+    // One wave of each 64-row tile records the decisions on its live tiles:
+    // bit t % 64 of rec (a wave-uniform value) for tile t, written to the
+    // bitmap a byte per lane and tile when a group of 64 tiles is complete,
+    // and at the end (a store per tile cost 8%).  The buffer resource ends
+    // at the wave's last live tile, so the range check drops the rest.
+    const int records = SKIP && ((slot / p.gw) & 1) == 0 ? 1 : 0;
+    uint64_t rec = 0;
+    auto record = [&](int t, int sk) { rec |= (uint64_t)(sk & records) << (t & 63); };
     auto flush_skips = [&](int t0) {
       uint8_t* row = p.skip_map == nullptr
                          ? nullptr
                          : p.skip_map + (((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT;
       const auto rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row ? wave_tiles : 0, kBufferFlags);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_buffer_store_b8(skip_lds[wave][i * 64 + lane], rs, t0 + i * 64 + lane, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)((rec >> lane) & 1), rs, t0 + lane, 0, 0);
+      skipped += (unsigned)__builtin_popcountll(rec);
+      rec = 0;
     };
-    // a full row of decisions is written in the phase of its last tile
-    auto flush_due = [&](int t) { return records && t < wave_tiles && (t & 255) == 255; };
+    // a full group of 64 decisions is written in the phase of its last tile
+    auto flush_due = [&](int t) { return records && t < wave_tiles && (t & 63) == 63; };
 
     // The last phase pair of the item: P.V of its last tile, then a VALU
     // phase with no tile work left, which takes the epilogue and, when the
@@ -806,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       if (do_pv) pv(n_tiles - 1, pk);
       block_barrier();
       if constexpr (SKIP) {
-        if (records && wave_tiles > 0) flush_skips((wave_tiles - 1) & ~255);  // the last row
+        if (records && (wave_tiles & 63) != 0) flush_skips((wave_tiles - 1) & ~63);  // the last group
         if (lane == 0 && skipped && p.skip_count)
           atomicAdd(p.skip_count, (unsigned long long)skipped);
       }
@@ -815,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       static_assert(4 * 32 * D * 2 <= T::STAGE, "four output slices must fit in a stage");
       static_assert(2 * 4 * 32 * D * 2 <= T::NST * T::KT, "eight output slices must fit in the K ring");
       // block skip: group g's slices in the K ring, free once the last Q.K^T is done
-      const uint32_t slice = (SKIP ? (uint32_t)grp * (4 * 32 * D * 2)
+      const uint32_t slice = (SKIP ? T::KRING + (uint32_t)grp * (4 * 32 * D * 2)
                                    : ((ring + n_tiles + 2 + grp) % T::NST) * T::STAGE) +
                              (wave & 3) * (32 * D * 2);
       LDS_AS unsigned char* ost = smem + slice;
@@ -931,26 +946,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     } else {
       // Block skip, in the same ping-pong, with the V load gated on the
       // decisions.  In its VALU phase j a wave takes the row maxima of tile
-      // j and votes; a skipped tile loses its softmax there and its P.V
-      // later; the running max of the decisions (m_true) takes every tile,
-      // skipped or not.  V tile j is copied in that phase by a group that
-      // keeps it (vote_collect), so it is known to be needed before it is
-      // loaded.  To give that copy a full phase pair to land, P.V of tile j
-      // runs in MFMA phase j+2 (not j+1): the P of two tiles are held (pkA
-      // for even tiles, pkB for odd ones), V tiles sit in a three-stage ring
-      // (V tile j overwrites tile j-3, whose last reader finished in MFMA
-      // phase j-1), and the copying group waits for them at the end of its
-      // VALU phase j+1.  K tiles sit in their own four-stage ring; group 1
-      // copies tile j+3 in its VALU phase j and waits for it at the end of
-      // its VALU phase j+1, before either group's Q.K^T of it.  In the
-      // common case of a tile both groups keep, group 0 copies its V and
-      // group 1 the K of a later tile, so the two phases issue about the
-      // same number of copies.
+      // j and votes; a skipped tile loses its exponentials there and its
+      // P.V later; the running max of the decisions (m_true) takes every
+      // tile, skipped or not.  V tile j is copied in that phase by a group
+      // that keeps it (vote_collect), so it is known to be needed before it
+      // is loaded.  To give that copy a full phase pair to land, P.V of tile
+      // j runs in MFMA phase j+2 (not j+1): the P of two tiles are held (pkA
+      // for even tiles, pkB for odd ones), V tile j overwrites tile j-4 in
+      // the V ring (its last reader finished in MFMA phase j-2), and the
+      // copying group waits for it at the end of its VALU phase j+1.  K tiles
+      // sit in their own four-stage ring; group 1 copies tile j+3 in its VALU
+      // phase j and waits for it at the end of its VALU phase j+1, before
+      // either group's Q.K^T of it.  In the common case of a tile both groups
+      // keep, group 0 copies its V and group 1 the K of a later tile, so the
+      // two phases issue about the same number of copies.  Each wave's
+      // number of copies in flight is fixed up to whether V was copied, so
+      // the wait that ends a steady phase is a choice of two counts.
       uint32_t pkA[2][8], pkB[2][8];
-      bool keepA = false, keepB = false;  // P.V due for the tile whose P is in pkA / pkB
+      int keepA = 0, keepB = 0;  // P.V due for the tile whose P is in pkA / pkB
       if (lane == 0) {
-        vote_lds[0][wave] = -2;
-        vote_lds[1][wave] = -2;
+        vote_lds[wave] = -2;
+        vote_lds[kWaves + wave] = -2;
       }
       block_barrier();
       if (grp == 1) {
@@ -960,42 +976,55 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       // one phase pair; pk holds the P of tile j-2 (read in the MFMA phase)
       // and receives that of tile j; keep likewise.  STEADY: every step is
       // present and no mask is needed (the steady-state copy of the body).
-      auto phase = [&](int j, uint32_t (*pk)[8], bool& keep, auto steady_tag) {
+      auto phase = [&](int j, uint32_t (*pk)[8], int& keep, auto steady_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
         if (STEADY ? keep : (j >= 2 && keep)) pv(j - 2, pk);
         if (STEADY || j < wave_tiles) qk(j, sc);
         block_barrier();
         apply_pending();
-        int inflight = 0;  // vector-memory operations issued in this phase
-        keep = false;
+        int loads = 0;  // copies (vector-memory loads) issued in this phase
+        int copyv = 0;
+        keep = 0;
         if (STEADY || j < n_tiles) {
-          const float tmx = STEADY ? tile_max(sc) : (j < wave_tiles ? row_max(j, sc) : -INFINITY);
-          const bool mine = vote_publish(j, tmx, STEADY || j < wave_tiles);
+          const bool live = STEADY || j < wave_tiles;
+          const float tmx = STEADY ? tile_max(sc) : (live ? row_max(j, sc) : -INFINITY);
+          const int mine = vote_publish(j, tmx, live);
           if (grp == 1 && (STEADY || j + 3 < n_tiles)) {
             issue_k(j + 3, STEADY);
-            inflight += kb_hi ? KB_HI : KB_LO;
+            loads += T::KPW;
           }
-          bool copyv, lost;
-          const bool sk = vote_collect(j, mine, copyv, lost);
-          if (flush_due(j)) {
-            flush_skips(j - 255);
-            inflight += 4;
-          }
+          // (the exponentials follow the decision; started ahead of it, by
+          // a wave whose own rows keep the tile, they measured slower)
+          int lost;
+          const int sk = vote_collect(j, mine, copyv, lost);
+          keep = live ? sk ^ 1 : 0;
+          if (keep) softmax(sc, tmx, pk);
+          if (live) record(j, sk);
+          if (flush_due(j)) flush_skips(j & ~63);
           if (copyv) {
             if (__builtin_expect(lost, 0)) {
               issue_v_all(j);
               wait_vmem<0>();
-              inflight = 0;
+              loads = 0;
             } else {
               issue_v(j, STEADY);
-              inflight += T::VPW;
+              loads += T::VPW;
             }
           }
           m_true = fmaxf(m_true, tmx);
-          keep = (STEADY || j < wave_tiles) && !sk;
-          if (keep) softmax(sc, tmx, pk);
         }
-        wait_vmem_upto(inflight);
+        // Wait until only this phase's copies are in flight (loads complete
+        // in order; the bitmap stores need no wait here).  The steady phase
+        // knows its count up to whether V was copied.
+        if constexpr (STEADY) {
+          if (grp == 0) {
+            if (copyv) wait_vmem<T::VPW>(); else wait_vmem<0>();
+          } else {
+            if (copyv) wait_vmem<T::KPW + T::VPW>(); else wait_vmem<T::KPW>();
+          }
+        } else {
+          wait_vmem_upto(loads);
+        }
         block_barrier();
       };
       using Gen = std::integral_constant<bool, false>;
@@ -1033,7 +1062,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
 template <int D, bool CAUSAL, bool SKIP, bool PAGED = false>
 hipError_t launch_one(const Params& p, int grid, hipStream_t stream) {
   auto kern = prefill_bf16_kernel<D, CAUSAL, SKIP, PAGED>;
-  constexpr size_t lds = SKIP ? Tile<D>::skip_lds_bytes : Tile<D>::lds_bytes;
+  constexpr size_t lds = Tile<D>::lds_bytes;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
