@@ -247,13 +247,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     const int kvh = bk % p.Hkv, b = bk / p.Hkv;
     // Waves w and w+4 share a SIMD and run the tile loop half an iteration
     // apart (see below), so they get adjacent 32-row slots: equal causal tile
-    // counts keep both busy to the end.  With block skip, the two waves of a
-    // 64-row skip tile (slots s and s ^ gw) must run in the same half; this
-    // mapping gives that for gw >= 2, and slot = wave (pairing waves 2k and
-    // 2k+1) for gw == 1.
-    const int slot = (SKIP && p.gw == 1) ? wave : ((wave & 3) << 1) | (wave >> 2);
-    const int pslot = slot ^ p.gw;  // block skip: the other half of this skip tile
-    const int pwave = (SKIP && p.gw == 1) ? pslot : ((pslot & 1) << 2) | (pslot >> 1);
+    // counts keep both busy to the end.  With block skip they hold the two
+    // halves of one 64-row skip tile (same head, rows r .. r+31 and r+32 ..
+    // r+63), which the decisions rely on (see the block-skip loop); for
+    // gw == 1 that is the same mapping.
+    const int kq = wave & 3;
+    const int slot = SKIP ? (kq % p.gw) + p.gw * (2 * (kq / p.gw) + (wave >> 2)) : (kq << 1) | (wave >> 2);
     const int head = kvh * p.G + sub * p.gw + (slot % p.gw);
     const int row0 = qblk * p.rows_per_wg;
     const int q0 = row0 + (slot / p.gw) * 32;
@@ -444,30 +443,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       }
     };
     // Block skip: K and V tiles are copied separately, each by one wave
-    // group and dealt round robin to its four waves: group 1 copies every K
-    // tile (tile j+3 in its VALU phase j), the group that copies a V tile is
-    // chosen by the decisions (see vote_collect).  Every group-1 wave issues
+    // group and dealt round robin to its four waves: group 0 copies every K
+    // tile (tile j+3 in its VALU phase j), group 1 the V tiles that the
+    // decisions keep (see the block-skip loop).  Every group-0 wave issues
     // KPW blocks of a K tile: a wave with one block fewer copies its last
     // block twice (the same bytes to the same place), so that its count of
     // copies in flight, and with it the wait at the end of a phase, is fixed.
     // Slot g of a block is row g / SL, chunk g % SL, as above; keys past the
     // end are clamped to the last key.
-    const int kq = wave & 3;
     const int kb_last = kq + 4 * (T::KPW - 1) < T::KSL ? kq + 4 * (T::KPW - 1) : kq + 4 * (T::KPW - 2);
     auto kblk = [&](int j) { return j == T::KPW - 1 ? kb_last : kq + 4 * j; };
     auto slot_off = [&](int g, int sl) -> uint32_t {
       const int r = g / sl, c = g % sl;
       return (uint32_t)r * T::RB + (c < T::CH ? c : 0) * 16;
     };
-    // a wave's own copy offsets: K blocks in group 1, V blocks in group 0
-    // (group 1 copies a V tile only when group 0 does not need it, and then
-    // forms the offsets as it goes)
+    // a wave's own copy offsets: K blocks in group 0, V blocks in group 1
     constexpr int NOFF = T::KPW > T::VPW ? T::KPW : T::VPW;
     uint32_t coff[SKIP ? NOFF : 1];
     if constexpr (SKIP) {
 #pragma unroll
       for (int j = 0; j < NOFF; ++j)
-        coff[j] = grp == 1 ? slot_off(kblk(j < T::KPW ? j : 0) * 64 + lane, T::KSL)
+        coff[j] = grp == 0 ? slot_off(kblk(j < T::KPW ? j : 0) * 64 + lane, T::KSL)
                            : slot_off((kq + 4 * j) * 64 + lane, T::VSL);
     }
     // offset of slot g of a block array with sl slots per row, with rows past
@@ -477,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       return o - (uint32_t)(r - min(r, lim)) * T::RB;
     };
     // (whole: the caller knows that tile t has all BN keys)
-    auto issue_k = [&](int t, bool whole) {  // a group-1 wave's KPW blocks of K tile t
+    auto issue_k = [&](int t, bool whole) {  // a group-0 wave's KPW blocks of K tile t
       const uint32_t st = smem_base + k_stage(t);
       const int key0 = t * BN;
       const uint16_t* src = Kg + (size_t)key0 * D;
@@ -492,18 +488,18 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         }
       }
     };
-    auto issue_v = [&](int t, bool whole) {  // this wave's VPW blocks of V tile t (its group copies it)
+    auto issue_v = [&](int t, bool whole) {  // a group-1 wave's VPW blocks of V tile t
       const uint32_t st = smem_base + v_stage(t);
       const int key0 = t * BN;
       const uint16_t* src = Vg + (size_t)key0 * D;
-      if (grp == 0 && (whole || key0 + BN <= S)) {
+      if (whole || key0 + BN <= S) {
 #pragma unroll
         for (int j = 0; j < T::VPW; ++j) dma16(src, coff[j], st + ((wave & 3) + 4 * j) * 1024);
       } else {
 #pragma unroll
         for (int j = 0; j < T::VPW; ++j) {
           const int i = (wave & 3) + 4 * j, g = i * 64 + lane;
-          dma16(src, clamp_off(slot_off(g, T::VSL), g, T::VSL, S - 1 - key0), st + i * 1024);
+          dma16(src, clamp_off(coff[j], g, T::VSL, S - 1 - key0), st + i * 1024);
         }
       }
     };
@@ -538,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       // places no vector-memory waits of its own inside the loop, where they
       // would also drain the tile prefetches.
       if constexpr (SKIP) {
-        if (grp == 1) {
+        if (grp == 0) {
           issue_k(0, false);
           if (n_tiles > 1) issue_k(1, false);
         }
@@ -715,89 +711,58 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     };
-    // block skip: this wave's vote on key tile t (are all 32 of its rows
-    // negligible?), published in LDS.  The other waves of the wave group run
-    // the same phase, so their votes on t arrive within a few instructions;
-    // vote_collect waits for the group's four (the other wave of this
-    // wave's 64-row tile is among them).  Work that does not depend on the
-    // decision sits between publish and collect, hiding the LDS round trip.
-    // V tile t is copied by group 0 if one of its 64-row tiles keeps t, else
-    // by group 1 if one of its tiles does (group 1 runs its phase after group
-    // 0's and sees group 0's votes); it is not copied at all when every tile
-    // of the workgroup skips t.  The wait is bounded: a wave whose group's
-    // votes do not all arrive keeps the tile (always exact), republishes its
-    // own vote as "keep" before the phase's closing barrier (so group 1 knows
-    // that group 0 needs the tile), and copies the whole V tile itself (lost
-    // = true).  Votes on even and odd tiles use separate slots, so a slot is
-    // rewritten only after every wave has read it (two barriers later).
-    // Lane 0 writes the vote; the other lanes of the same write land in a
-    // scratch area, which spares switching lanes off and on.
-    // The decision values below are wave-uniform ints built from ballots
-    // (bit w of a ballot over lanes 0-7 = wave w), so that they stay in
-    // scalar registers.
+    // Block skip: each wave votes on key tile t (are all 32 of its rows
+    // negligible?) in its VALU phase t, into an LDS slot of its own (one set
+    // for even tiles, one for odd ones); a 64-row tile is skipped when both
+    // of its waves, w and w+4, vote so.  The votes need no waiting: group 1
+    // reads group 0's votes on t in its own VALU phase t, which follows
+    // group 0's behind a barrier, and group 0 reads its partner's vote on t
+    // in its VALU phase t+1, behind the next barrier.  A slot is rewritten
+    // two tiles later, after both readers are done.  Lane 0 writes the vote;
+    // the other lanes of the same write land in a scratch area, which spares
+    // switching lanes off and on.
     LDS_AS int* const vote_w =
         (LDS_AS int*)&vote_lds[0] + (lane == 0 ? wave : 2 * kWaves + lane - 1);
     // lanes whose query row is past the end vote "negligible" on every tile
     const uint64_t rows_out = __ballot(q0 + n >= S);
-    // 1 if every row of this wave is negligible on tile t
+    // 1 if every row of this wave is negligible on tile t (so when not live)
     auto vote_publish = [&](int t, float tmx_t, bool live) -> int {
       int all_neg = 1;
       if (live) {
         const bool neg = (tmx_t == -INFINITY) | ((m_true > 0.5f * kUnset) & (tmx_t - m_true < thr));
         all_neg = (__ballot(neg) | rows_out) == ~0ull ? 1 : 0;
       }
-      __hip_atomic_store(vote_w + (t & 1) * kWaves, (t << 1) | all_neg, __ATOMIC_RELAXED,
+      __hip_atomic_store(vote_w + (t & 1) * kWaves, all_neg, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_WORKGROUP);
       return all_neg;
     };
-    // lanes 0-7 each read one wave's vote; ballots then test the tags and
-    // gather the verdicts
-    const LDS_AS int* const vote_r = (const LDS_AS int*)&vote_lds[0] + (lane & (kWaves - 1));
-    const uint32_t wait_mask = grp == 0 ? 0x0Fu : 0xFFu;  // group 1 also waits for group 0's votes
-    // 1 if tile t is skipped; copyv = 1 if this wave's group copies V tile t
-    auto vote_collect = [&](int t, int all_neg, int& copyv, int& lost) -> int {
-      uint32_t keeps = 0, ready = 0;
-      for (int spin = 0; spin < (1 << 16); ++spin) {
-        const int d = *(volatile const LDS_AS int*)(vote_r + (t & 1) * kWaves) ^ (t << 1);
-        keeps = (uint32_t)__ballot(d == 0) & 0xFFu;  // waves with a row that keeps t
-        ready = (uint32_t)__ballot((unsigned)d <= 1u) & wait_mask;
-        if (ready == wait_mask) break;
-      }
-      lost = ready != wait_mask ? 1 : 0;
-      // does a 64-row tile of group 0 keep t?  then group 0 copies V tile t;
-      // else group 1 does if one of its tiles keeps it
-      const int need0 = (keeps & 0x0Fu) != 0 ? 1 : 0, need1 = (keeps & 0xF0u) != 0 ? 1 : 0;
-      copyv = grp == 0 ? need0 : need1 & (need0 ^ 1);
-      const int other_neg = ((keeps >> pwave) & 1u) ^ 1u;
-      if (__builtin_expect(lost, 0)) {
-        // the wait ran out: keep the tile, say so, and copy V tile t
-        copyv = 1;
-        __hip_atomic_store(vote_w + (t & 1) * kWaves, t << 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        return 0;
-      }
-      return all_neg & other_neg;
-    };
-    // One wave of each 64-row tile records the decisions on its live tiles:
-    // bit t % 64 of rec (a wave-uniform value) for tile t, written to the
-    // bitmap a byte per lane and tile when a group of 64 tiles is complete,
-    // and at the end (a store per tile cost 8%).  The buffer resource ends
-    // at the wave's last live tile, so the range check drops the rest.
-    const int records = SKIP && ((slot / p.gw) & 1) == 0 ? 1 : 0;
+    // group 1: lanes 0-3 read group 0's votes on tile t (lane w = wave w)
+    const LDS_AS int* const vote_r0 = (const LDS_AS int*)&vote_lds[0] + (lane & 3);
+    auto read_votes0 = [&](int t) -> int { return *(volatile const LDS_AS int*)(vote_r0 + (t & 1) * kWaves); };
+    // group 0: its partner's (wave + 4) vote on tile t, in every lane
+    const LDS_AS int* const vote_rp = (const LDS_AS int*)&vote_lds[0] + wave + 4;
+    auto read_partner = [&](int t) -> int { return *(volatile const LDS_AS int*)(vote_rp + (t & 1) * kWaves); };
+    // Group 1 records the decisions on its 64-row tile's live tiles (it
+    // learns each one in the tile's phase): bit t % 64 of rec (a
+    // wave-uniform value) for tile t, written to the bitmap a byte per lane
+    // and tile when a group of 64 tiles is complete, and at the end (a store
+    // per tile cost 8%).  The buffer resource ends at the tile row's last
+    // live tile (rec_tiles), so the range check drops the rest.
+    const int records = SKIP && grp == 1 && q0 - 32 < Sq ? 1 : 0;
+    const int rec_tiles = records ? (off + min(Sq - 1, q0 + 31)) / BN + 1 : 0;
     uint64_t rec = 0;
     auto record = [&](int t, int sk) { rec |= (uint64_t)(sk & records) << (t & 63); };
     auto flush_skips = [&](int t0) {
       uint8_t* row = p.skip_map == nullptr
                          ? nullptr
                          : p.skip_map + (((size_t)b * p.Hq + head) * p.nT + q0 / BN) * p.nT;
-      const auto rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row ? wave_tiles : 0, kBufferFlags);
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row ? rec_tiles : 0, kBufferFlags);
       __builtin_amdgcn_raw_buffer_store_b8((uint8_t)((rec >> lane) & 1), rs, t0 + lane, 0, 0);
       skipped += (unsigned)__builtin_popcountll(rec);
       rec = 0;
     };
     // a full group of 64 decisions is written in the phase of its last tile
-    auto flush_due = [&](int t) { return records && t < wave_tiles && (t & 63) == 63; };
+    auto flush_due = [&](int t) { return records && t < rec_tiles && (t & 63) == 63; };
 
     // The last phase pair of the item: P.V of its last tile, then a VALU
     // phase with no tile work left, which takes the epilogue and, when the
@@ -821,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       if (do_pv) pv(n_tiles - 1, pk);
       block_barrier();
       if constexpr (SKIP) {
-        if (records && (wave_tiles & 63) != 0) flush_skips((wave_tiles - 1) & ~63);  // the last group
+        if (records && (rec_tiles & 63) != 0) flush_skips((rec_tiles - 1) & ~63);  // the last group
         if (lane == 0 && skipped && p.skip_count)
           atomicAdd(p.skip_count, (unsigned long long)skipped);
       }
@@ -945,104 +910,114 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       finish(n_tiles - 1 < wave_tiles, pk);
     } else {
       // Block skip, in the same ping-pong, with the V load gated on the
-      // decisions.  In its VALU phase j a wave takes the row maxima of tile
-      // j and votes; a skipped tile loses its exponentials there and its
-      // P.V later; the running max of the decisions (m_true) takes every
-      // tile, skipped or not.  V tile j is copied in that phase by a group
-      // that keeps it (vote_collect), so it is known to be needed before it
-      // is loaded.  To give that copy a full phase pair to land, P.V of tile
-      // j runs in MFMA phase j+2 (not j+1): the P of two tiles are held (pkA
-      // for even tiles, pkB for odd ones), V tile j overwrites tile j-4 in
-      // the V ring (its last reader finished in MFMA phase j-2), and the
-      // copying group waits for it at the end of its VALU phase j+1.  K tiles
-      // sit in their own four-stage ring; group 1 copies tile j+3 in its VALU
-      // phase j and waits for it at the end of its VALU phase j+1, before
-      // either group's Q.K^T of it.  In the common case of a tile both groups
-      // keep, group 0 copies its V and group 1 the K of a later tile, so the
-      // two phases issue about the same number of copies.  Each wave's
-      // number of copies in flight is fixed up to whether V was copied, so
-      // the wait that ends a steady phase is a choice of two counts.
+      // decisions.  Waves w (group 0) and w+4 (group 1) hold the two halves
+      // of one 64-row tile, and group 1 runs half an iteration behind.
+      //  * Group 1, in its VALU phase j, reads group 0's votes on tile j
+      //    (published in group 0's phase j, before the barrier), so it knows
+      //    its tile's decision at once: a skipped tile loses its
+      //    exponentials.  It copies V tile j when a group-0 half keeps it (a
+      //    quarter per wave, as soon as the votes are read) or, failing
+      //    that, when its own half does (the whole tile, from that wave).
+      //    It waits for the copy at the end of its next MFMA phase, before
+      //    either group's P.V of tile j.
+      //  * Group 0 copies the K tiles (tile j+3 in its VALU phase j), runs
+      //    the exponentials of every live tile, and learns the decision on
+      //    tile j from its partner's vote in its VALU phase j+1; the row sum
+      //    of tile j waits until then (lpend) and is added, if the tile is
+      //    kept, before that phase's rescale, which keeps the arithmetic of
+      //    the dense kernel.
+      //  * P.V of tile j runs in MFMA phase j+2 for both groups (so the P of
+      //    two tiles are held: pkA for even tiles, pkB for odd ones); V tile
+      //    j overwrites tile j-4 in the V ring, whose last reader finished
+      //    in MFMA phase j-2.  K tile j+3 overwrites tile j-1, read last by
+      //    group 1's Q.K^T in the MFMA phase that ran beside group 0's VALU
+      //    phase j-1.
+      //  * The running max of the decisions (m_true) takes every tile,
+      //    skipped or not.
       uint32_t pkA[2][8], pkB[2][8];
       int keepA = 0, keepB = 0;  // P.V due for the tile whose P is in pkA / pkB
-      if (lane == 0) {
-        vote_lds[wave] = -2;
-        vote_lds[kWaves + wave] = -2;
-      }
+      int mine_prev = 1, live_prev = 0;  // group 0: its vote on, and rows in, tile j-1
+      float lpend = 0.f;                 // group 0: row sum of tile j-1, added once it is kept
       block_barrier();
-      if (grp == 1) {
+      if (grp == 0) {
         if (2 < n_tiles) issue_k(2, false);
+      } else {
         block_barrier();
       }
       // one phase pair; pk holds the P of tile j-2 (read in the MFMA phase)
-      // and receives that of tile j; keep likewise.  STEADY: every step is
-      // present and no mask is needed (the steady-state copy of the body).
-      auto phase = [&](int j, uint32_t (*pk)[8], int& keep, auto steady_tag) {
+      // and receives that of tile j; keep is the flag of that buffer's tile
+      // and keepo the other's.  STEADY: every step is present and no mask is
+      // needed (the steady-state copy of the body).
+      auto phase = [&](int j, uint32_t (*pk)[8], int& keep, int& keepo, auto steady_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
         if (STEADY ? keep : (j >= 2 && keep)) pv(j - 2, pk);
         if (STEADY || j < wave_tiles) qk(j, sc);
+        if (grp == 1) wait_vmem<0>();  // V tile j-1, before group 0's P.V of it
         block_barrier();
         apply_pending();
-        int loads = 0;  // copies (vector-memory loads) issued in this phase
-        int copyv = 0;
-        keep = 0;
-        if (STEADY || j < n_tiles) {
-          const bool live = STEADY || j < wave_tiles;
-          const float tmx = STEADY ? tile_max(sc) : (live ? row_max(j, sc) : -INFINITY);
-          const int mine = vote_publish(j, tmx, live);
-          if (grp == 1 && (STEADY || j + 3 < n_tiles)) {
+        const bool live = STEADY || j < wave_tiles;
+        if (grp == 0) {
+          const int pvote = j >= 1 ? read_partner(j - 1) : 1;
+          int loads = 0;  // copies issued in this phase
+          if (STEADY || j + 3 < n_tiles) {
             issue_k(j + 3, STEADY);
-            loads += T::KPW;
+            loads = T::KPW;
           }
-          // (the exponentials follow the decision; started ahead of it, by
-          // a wave whose own rows keep the tile, they measured slower)
-          int lost;
-          const int sk = vote_collect(j, mine, copyv, lost);
+          float tmx = -INFINITY;
+          int mine = 1;
+          if (STEADY || j < n_tiles) {
+            tmx = STEADY ? tile_max(sc) : (live ? row_max(j, sc) : -INFINITY);
+            mine = vote_publish(j, tmx, live);
+          }
+          // tile j-1 decided: both halves negligible skips it
+          keepo = live_prev & (mine_prev & __builtin_amdgcn_readfirstlane(pvote) ^ 1);
+          if (keepo) l += lpend;
+          keep = live ? 1 : 0;  // for now; decided in the next phase
+          lpend = 0.f;
+          if (live) {
+            rescale(tmx);
+            lpend = exps(sc, pk, -m_used);
+          }
+          mine_prev = mine;
+          live_prev = live ? 1 : 0;
+          if (STEADY || j < n_tiles) m_true = fmaxf(m_true, tmx);
+          if constexpr (STEADY) wait_vmem<T::KPW>(); else wait_vmem_upto(loads);
+        } else if (STEADY || j < n_tiles) {
+          const int v0 = read_votes0(j);
+          const float tmx = STEADY ? tile_max(sc) : (live ? row_max(j, sc) : -INFINITY);
+          const uint32_t negs0 = (uint32_t)__ballot(v0 != 0) & 0x0Fu;  // group 0's negligible halves
+          const int keep0 = negs0 != 0x0Fu ? 1 : 0;                  // a group-0 half keeps tile j
+          if (keep0) issue_v(j, STEADY);
+          const int mine = vote_publish(j, tmx, live);
+          const int sk = mine & (int)((negs0 >> kq) & 1u);
           keep = live ? sk ^ 1 : 0;
-          if (keep) softmax(sc, tmx, pk);
-          if (live) record(j, sk);
-          if (flush_due(j)) flush_skips(j & ~63);
-          if (copyv) {
-            if (__builtin_expect(lost, 0)) {
-              issue_v_all(j);
-              wait_vmem<0>();
-              loads = 0;
-            } else {
-              issue_v(j, STEADY);
-              loads += T::VPW;
-            }
+          if (keep) {
+            softmax(sc, tmx, pk);
+            if (!keep0) issue_v_all(j);  // only this half keeps V tile j
           }
+          if (j < rec_tiles) record(j, sk);
+          if (flush_due(j)) flush_skips(j & ~63);
           m_true = fmaxf(m_true, tmx);
         }
-        // Wait until only this phase's copies are in flight (loads complete
-        // in order; the bitmap stores need no wait here).  The steady phase
-        // knows its count up to whether V was copied.
-        if constexpr (STEADY) {
-          if (grp == 0) {
-            if (copyv) wait_vmem<T::VPW>(); else wait_vmem<0>();
-          } else {
-            if (copyv) wait_vmem<T::KPW + T::VPW>(); else wait_vmem<T::KPW>();
-          }
-        } else {
-          wait_vmem_upto(loads);
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the vote is in LDS before the barrier
         block_barrier();
       };
       using Gen = std::integral_constant<bool, false>;
       using Ste = std::integral_constant<bool, true>;
-      // steady phases: 2 <= j < j_ss (P.V of j-2, Q.K^T of j, the K copy of
-      // tile j+3, no mask, and K tile j+3 and V tile j not the last tile, so
+      // steady phases: 2 <= j < j_ss (P.V of j-2, Q.K^T of j, the copies of
+      // K tile j+3 and V tile j, no mask, and neither the last tile, so
       // whole), run in pairs so that each P buffer stays in fixed registers
       const int j_ss = min(min(wave_tiles, first_masked), n_tiles - 4);
-      phase(0, pkA, keepA, Gen{});
-      if (1 <= n_tiles) phase(1, pkB, keepB, Gen{});
+      phase(0, pkA, keepA, keepB, Gen{});
+      if (1 <= n_tiles) phase(1, pkB, keepB, keepA, Gen{});
       int j = 2;
       for (; j + 1 < j_ss; j += 2) {
-        phase(j, pkA, keepA, Ste{});
-        phase(j + 1, pkB, keepB, Ste{});
+        phase(j, pkA, keepA, keepB, Ste{});
+        phase(j + 1, pkB, keepB, keepA, Ste{});
       }
       for (; j <= n_tiles; j += 2) {
-        phase(j, pkA, keepA, Gen{});
-        if (j + 1 <= n_tiles) phase(j + 1, pkB, keepB, Gen{});
+        phase(j, pkA, keepA, keepB, Gen{});
+        if (j + 1 <= n_tiles) phase(j + 1, pkB, keepB, keepA, Gen{});
       }
       // MFMA phase n_tiles + 1: P.V of the last tile
       if ((n_tiles + 1) & 1) {
