@@ -40,10 +40,11 @@
 //    each item's last phase writes its output through LDS as whole rows and
 //    copies the next item's Q and first two K/V tiles.
 //  * Block skip: after the row maxima of a tile each wave votes whether its
-//    rows are negligible; a 64x64 tile both of whose waves vote so loses its
-//    exponentials and its P.V, and the V tile is copied from memory only if
-//    some 64-row tile of the workgroup keeps it (P.V runs one tile later to
-//    give that copy time to land).
+//    rows are negligible; a 64x64 tile, whose two halves sit on the two
+//    waves of one SIMD, is skipped when both vote so: it loses its P.V and
+//    (in the wave that learns the decision first) its exponentials, and the
+//    V tile is copied from memory only if some 64-row tile of the workgroup
+//    keeps it (P.V runs one tile later to give that copy time to land).
 #include "attn_internal.h"
 
 #include <math.h>
