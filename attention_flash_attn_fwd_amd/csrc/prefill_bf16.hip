@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     };
     // Block skip: K and V tiles are copied separately, each by one wave
     // group and dealt round robin to its four waves: group 0 copies every K
-    // tile (tile j+3 in its VALU phase j), group 1 the V tiles that the
+    // tile (tile j+2 in its VALU phase j), group 1 the V tiles that the
     // decisions keep (see the block-skip loop).  Every group-0 wave issues
     // KPW blocks of a K tile: a wave with one block fewer copies its last
     // block twice (the same bytes to the same place), so that its count of
@@ -597,6 +597,18 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // Q.K^T of keys kb*32 .. kb*32+31 of tile t alone, into acc (block
+    // skip: the recompute of a tile, one 32-key half at a time)
+    auto qk_half = [&](int t, int kb, f32x16& acc_) {
+      const LDS_AS unsigned char* kp = smem + k_stage(t) + k_base + kb * 32 * T::RK;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(kp + ks * 32);
+        acc_ = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc_, 0, 0, 0);
+      }
     };
     // mask (diagonal and ragged tiles only) and scaled row max of a score tile
     auto mask_tile = [&](int t, f32x16* sc) {
@@ -921,35 +933,36 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       //    that, when its own half does (the whole tile, from that wave).
       //    It waits for the copy at the end of its next MFMA phase, before
       //    either group's P.V of tile j.
-      //  * Group 0 copies the K tiles (tile j+3 in its VALU phase j), runs
-      //    the exponentials of every live tile, and learns the decision on
-      //    tile j from its partner's vote in its VALU phase j+1; the row sum
-      //    of tile j waits until then (lpend) and is added, if the tile is
-      //    kept, before that phase's rescale, which keeps the arithmetic of
-      //    the dense kernel.
+      //  * Group 0 copies the K tiles (tile j+2 in its VALU phase j, into
+      //    the stage of tile j-2), runs the exponentials of each live tile
+      //    on which its own rows are not all negligible (such a tile is
+      //    kept), and learns the decision on tile j from its partner's vote
+      //    in its VALU phase j+1; the row sum of tile j waits until then
+      //    (lpend) and is added, if the tile is kept, before that phase's
+      //    rescale, which keeps the arithmetic of the dense kernel.  A tile
+      //    kept only by the partner's half is recomputed then from K tile j,
+      //    still in its stage.
       //  * P.V of tile j runs in MFMA phase j+2 for both groups (so the P of
       //    two tiles are held: pkA for even tiles, pkB for odd ones); V tile
       //    j overwrites tile j-4 in the V ring, whose last reader finished
-      //    in MFMA phase j-2.  K tile j+3 overwrites tile j-1, read last by
+      //    in MFMA phase j-2.  K tile j+2 overwrites tile j-2, read last by
       //    group 1's Q.K^T in the MFMA phase that ran beside group 0's VALU
-      //    phase j-1.
+      //    phase j-2 (and by group 0's recompute in its phase j-1).
       //  * The running max of the decisions (m_true) takes every tile,
       //    skipped or not.
       uint32_t pkA[2][8], pkB[2][8];
       int keepA = 0, keepB = 0;  // P.V due for the tile whose P is in pkA / pkB
       int mine_prev = 1, live_prev = 0;  // group 0: its vote on, and rows in, tile j-1
+      int done_prev = 0;                 // group 0: the exponentials of tile j-1 were computed
       float lpend = 0.f;                 // group 0: row sum of tile j-1, added once it is kept
       block_barrier();
-      if (grp == 0) {
-        if (2 < n_tiles) issue_k(2, false);
-      } else {
-        block_barrier();
-      }
+      if (grp == 1) block_barrier();
       // one phase pair; pk holds the P of tile j-2 (read in the MFMA phase)
-      // and receives that of tile j; keep is the flag of that buffer's tile
-      // and keepo the other's.  STEADY: every step is present and no mask is
-      // needed (the steady-state copy of the body).
-      auto phase = [&](int j, uint32_t (*pk)[8], int& keep, int& keepo, auto steady_tag) {
+      // and receives that of tile j; keep is the flag of that buffer's tile,
+      // pko and keepo the other buffer and its flag.  STEADY: every step is
+      // present and no mask is needed (the steady-state copy of the body).
+      auto phase = [&](int j, uint32_t (*pk)[8], int& keep, uint32_t (*pko)[8], int& keepo,
+                       auto steady_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
         if (STEADY ? keep : (j >= 2 && keep)) pv(j - 2, pk);
         if (STEADY || j < wave_tiles) qk(j, sc);
@@ -960,8 +973,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
         if (grp == 0) {
           const int pvote = j >= 1 ? read_partner(j - 1) : 1;
           int loads = 0;  // copies issued in this phase
-          if (STEADY || j + 3 < n_tiles) {
-            issue_k(j + 3, STEADY);
+          if (STEADY || j + 2 < n_tiles) {
+            issue_k(j + 2, STEADY);
             loads = T::KPW;
           }
           float tmx = -INFINITY;
@@ -971,16 +984,48 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
             mine = vote_publish(j, tmx, live);
           }
           // tile j-1 decided: both halves negligible skips it
-          keepo = live_prev & (mine_prev & __builtin_amdgcn_readfirstlane(pvote) ^ 1);
-          if (keepo) l += lpend;
+          keepo = live_prev & ((mine_prev & __builtin_amdgcn_readfirstlane(pvote)) ^ 1);
+          if (keepo & done_prev) l += lpend;
+          const float m_before = m_used;
           keep = live ? 1 : 0;  // for now; decided in the next phase
           lpend = 0.f;
-          if (live) {
+          int done = 0;
+          if (live && !mine) {
             rescale(tmx);
             lpend = exps(sc, pk, -m_used);
+            done = 1;
+          }
+          if (keepo & (done_prev ^ 1)) {
+            // Tile j-1 is kept although every row of this half was
+            // negligible on it, so its exponentials were left out: its
+            // scores are formed again from K tile j-1, still in LDS (a
+            // 32-key half at a time), with the exponent reference of tile
+            // j-1, and its row sum joins l scaled to the current reference.
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              qk_half(j - 1, kb, sc[0]);
+              if (!STEADY && j - 1 >= first_masked) {
+                const int c0 = (j - 1) * BN + kb * 32, qi = q0 + n;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const int key = c0 + (i >> 2) * 8 + hf * 4 + (i & 3);
+                  if (key >= S || key > off + qi) sc[0][i] = -INFINITY;
+                }
+              }
+#pragma unroll
+              for (int i = 0; i < 16; i += 2)
+                pko[kb][i >> 1] = pack_bf16(fast_exp2(fmaf(sc[0][i], sl2, -m_before)),
+                                            fast_exp2(fmaf(sc[0][i + 1], sl2, -m_before)));
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pko[kb][i]), kOnes2, rs, false);
+            }
+            l += rs * fast_exp2(m_before - m_used);
           }
           mine_prev = mine;
           live_prev = live ? 1 : 0;
+          done_prev = done;
           if (STEADY || j < n_tiles) m_true = fmaxf(m_true, tmx);
           if constexpr (STEADY) wait_vmem<T::KPW>(); else wait_vmem_upto(loads);
         } else if (STEADY || j < n_tiles) {
@@ -1006,19 +1051,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       using Gen = std::integral_constant<bool, false>;
       using Ste = std::integral_constant<bool, true>;
       // steady phases: 2 <= j < j_ss (P.V of j-2, Q.K^T of j, the copies of
-      // K tile j+3 and V tile j, no mask, and neither the last tile, so
+      // K tile j+2 and V tile j, no mask, and neither the last tile, so
       // whole), run in pairs so that each P buffer stays in fixed registers
       const int j_ss = min(min(wave_tiles, first_masked), n_tiles - 4);
-      phase(0, pkA, keepA, keepB, Gen{});
-      if (1 <= n_tiles) phase(1, pkB, keepB, keepA, Gen{});
+      phase(0, pkA, keepA, pkB, keepB, Gen{});
+      if (1 <= n_tiles) phase(1, pkB, keepB, pkA, keepA, Gen{});
       int j = 2;
       for (; j + 1 < j_ss; j += 2) {
-        phase(j, pkA, keepA, keepB, Ste{});
-        phase(j + 1, pkB, keepB, keepA, Ste{});
+        phase(j, pkA, keepA, pkB, keepB, Ste{});
+        phase(j + 1, pkB, keepB, pkA, keepA, Ste{});
       }
       for (; j <= n_tiles; j += 2) {
-        phase(j, pkA, keepA, keepB, Gen{});
-        if (j + 1 <= n_tiles) phase(j + 1, pkB, keepB, keepA, Gen{});
+        phase(j, pkA, keepA, pkB, keepB, Gen{});
+        if (j + 1 <= n_tiles) phase(j + 1, pkB, keepB, pkA, keepA, Gen{});
       }
       // MFMA phase n_tiles + 1: P.V of the last tile
       if ((n_tiles + 1) & 1) {
