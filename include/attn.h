@@ -132,9 +132,7 @@ int attn_prefill_f32(const float* q, const float* k, const float* v, float* o, f
  * O and LSE are then exact attention over the keys of the tiles not skipped.
  * The V rows of key tile kt are not read from memory when every query tile
  * processed together with it (up to four query heads of the K/V group, 64
- * rows each) skips kt.  The exponentials of the first 32 rows of a tile are
- * computed before its decision is known and discarded if it is skipped; the
- * other 32 rows skip them.
+ * rows each) skips kt.
  *
  *   lambda        : 0 < lambda < 1
  *   tile          : must be 64

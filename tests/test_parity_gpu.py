@@ -493,6 +493,19 @@ def test_blockskip_stress_full_decisions(B, Hq, Hkv, S, D):
     _check_blockskip_all(w, 1e-3, f"stress B{B} Hq{Hq} Hkv{Hkv} S{S} D{D}", min_frac=0.02)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S,D", [
+    (1, 8, 2, 2048, 128),    # groups of 4 heads
+    (1, 4, 4, 1024, 128),    # one head per K/V group
+    (1, 4, 2, 1500, 64),     # D = 64, ragged last tile
+])
+def test_blockskip_split_tiles(B, Hq, Hkv, S, D):
+    """Tiles kept only through their second 32-row half: the wave holding the
+    first half skips its exponentials and recomputes the tile a phase later."""
+    say(f"block skip split tiles: B{B} Hq{Hq} Hkv{Hkv} S{S} D{D}")
+    w = blockskip_inputs(B, Hq, Hkv, S, D, seed=1107 + S, amplitude=16.0, boosted="split_tiles")
+    _check_blockskip_all(w, 1e-3, f"split tiles B{B} Hq{Hq} Hkv{Hkv} S{S} D{D}")
+
+
 def test_blockskip_small_lambda_equals_dense():
     say("block skip with lambda=1e-30 equals the dense kernel")
     w = blockskip_inputs(1, 4, 1, 700, 128, seed=1106, amplitude=12.0, boosted="second_half")

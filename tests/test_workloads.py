@@ -61,6 +61,30 @@ def test_blockskip_structure():
     assert abs(k[0, :, others, w.boost_dim].mean()) < 0.5
 
 
+def test_blockskip_split_tiles_halves_disagree():
+    """The split-tile input: on every key tile after the first, the first 32
+    rows of a 64-row query tile are all negligible (lambda = 1e-3) while the
+    last 32 are not, so the tile is kept only through its second half.
+    Checked with the decision rule in numpy (float64) on one head."""
+    import math
+    w = blockskip_inputs(1, 2, 1, 512, 128, seed=7, amplitude=16.0, boosted="split_tiles")
+    q = w.q.double().numpy()[0, 0]
+    k = w.k.double().numpy()[0, 0]
+    ln_lam = math.log(1e-3)
+    checked = 0
+    for qt in range(1, 8):
+        rows = np.arange(qt * 64, qt * 64 + 64)
+        s = w.scale * (q[rows] @ k[:(qt + 1) * 64].T)
+        s = np.where(np.arange((qt + 1) * 64)[None, :] <= rows[:, None], s, -np.inf)
+        tm = s.reshape(64, qt + 1, 64).max(axis=2)
+        mp = np.concatenate([np.full((64, 1), -np.inf), np.maximum.accumulate(tm, axis=1)[:, :-1]], axis=1)
+        neg = np.isneginf(tm) | (np.isfinite(mp) & (tm - mp < ln_lam))
+        for kt in range(1, qt + 1):
+            assert neg[:32, kt].all() and not neg[32:, kt].all(), (qt, kt)
+            checked += 1
+    assert checked == 28
+
+
 def test_named_configs_and_gqa_saving():
     assert CONFIGS["gqa_causal_s8192"]["Hq"] // CONFIGS["gqa_causal_s8192"]["Hkv"] == 4
     # the GQA page's 32-query-head / 8-group example: the K/V cache shrinks by 75%

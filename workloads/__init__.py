@@ -149,12 +149,34 @@ def blockskip_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, *, seed: int,
     ``boosted`` is "random_half" (S/2 positions drawn without replacement) or
     "second_half" (positions S/2 .. S-1, the stress variant).  The boost is
     added to the float32 sample before rounding to ``dtype``.
+
+    ``boosted="split_tiles"`` builds tiles whose two 32-row halves disagree:
+    key 0 is the only sink and every query row is boosted along u, and a
+    second coordinate k2 != k (w = e_k2, drawn after k) gets ``amplitude *
+    w`` on key 64t + 17 of every 64-key tile t and on the query rows r with
+    r % 64 >= 32.  Rows of the first half of each 64-row block then find
+    every key tile after the first negligible against key 0, while rows of
+    the second half do not (``n_sinks`` is ignored).
     """
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     kdim = int(rng.integers(0, D))
+    if boosted == "split_tiles":
+        kdim2 = (kdim + 1 + int(rng.integers(0, D - 1))) % D
+        sinks = np.array([0])
+        spots = np.arange(17, S, 64)
+        rows = np.arange(S)
+        k[:, :, sinks, kdim] += np.float32(amplitude)
+        q[:, :, :, kdim] += np.float32(amplitude)
+        k[:, :, spots, kdim2] += np.float32(amplitude)
+        q[:, :, rows[rows % 64 >= 32], kdim2] += np.float32(amplitude)
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        return PrefillInputs(to_dtype(q, dtype), to_dtype(k, dtype), to_dtype(v, dtype),
+                             B, Hq, Hkv, S, D, True, float(scale), dtype, seed,
+                             sink_rows=sinks, boosted_rows=rows, boost_dim=kdim)
     sinks = np.sort(rng.choice(S, size=min(n_sinks, S), replace=False))
     if boosted == "random_half":
         rows = np.sort(rng.choice(S, size=S // 2, replace=False))
