@@ -463,14 +463,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
     uint32_t coff[SKIP ? NOFF : 1];
     if constexpr (SKIP) {
 #pragma unroll
-      for (int j = 0; j < NOFF; ++j)
+      for (int j = 0; j < NOFF; ++j) {
         coff[j] = grp == 0 ? slot_off(kblk(j < T::KPW ? j : 0) * 64 + lane, T::KSL)
                            : slot_off((kq + 4 * j) * 64 + lane, T::VSL);
+        asm volatile("" : "+v"(coff[j]));  // kept whole (its parts cost registers)
+      }
     }
-    // offset of slot g of a block array with sl slots per row, with rows past
-    // lim clamped to row lim
-    auto clamp_off = [&](uint32_t o, int g, int sl, int lim) -> uint32_t {
-      const int r = g / sl;
+    // offset o of this lane's slot of block i of a block array with sl
+    // slots per row, with rows past lim clamped to row lim
+    auto clamp_off = [&](uint32_t o, int i, int sl, int lim) -> uint32_t {
+      // (the lane index passes through an empty asm so that the row is
+      // formed here, in the rare ragged copy, instead of being hoisted and
+      // kept for the whole item, which cost registers)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int r = (i * 64 + ln) / sl;
       return o - (uint32_t)(r - min(r, lim)) * T::RB;
     };
     // (whole: the caller knows that tile t has all BN keys)
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
 #pragma unroll
         for (int j = 0; j < T::KPW; ++j) {
           const int i = kblk(j);
-          dma16(src, clamp_off(coff[j], i * 64 + lane, T::KSL, S - 1 - key0), st + i * 1024);
+          dma16(src, clamp_off(coff[j], i, T::KSL, S - 1 - key0), st + i * 1024);
         }
       }
     };
@@ -499,8 +506,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       } else {
 #pragma unroll
         for (int j = 0; j < T::VPW; ++j) {
-          const int i = (wave & 3) + 4 * j, g = i * 64 + lane;
-          dma16(src, clamp_off(coff[j], g, T::VSL, S - 1 - key0), st + i * 1024);
+          const int i = (wave & 3) + 4 * j;
+          dma16(src, clamp_off(coff[j], i, T::VSL, S - 1 - key0), st + i * 1024);
         }
       }
     };
@@ -509,8 +516,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Params) {
       const int key0 = t * BN;
       const uint16_t* src = Vg + (size_t)key0 * D;
       for (int i = 0; i < T::VSL; ++i) {
-        const int g = i * 64 + lane;
-        dma16(src, clamp_off(slot_off(g, T::VSL), g, T::VSL, S - 1 - key0), st + i * 1024);
+        int g = i * 64 + lane;
+        asm volatile("" : "+v"(g));
+        dma16(src, clamp_off(slot_off(g, T::VSL), i, T::VSL, S - 1 - key0), st + i * 1024);
       }
     };
 
