@@ -374,6 +374,32 @@ def cmd_counters(a):
     print("\n".join(lines))
 
 
+def cmd_pmc(a):
+    """Counters per launch (mean over the last launches) of one kernel for
+    several runs: one run directory per label."""
+    labels = a.labels.split(",")
+    dirs = a.dirs.split(",")
+    counters = a.counters.split(",")
+    assert len(labels) == len(dirs)
+    lines = [a.title, "", "Command (repo root, TMPDIR=/tmp), for each run:", "  " + a.cmd, "",
+             f"Mean per launch over the last {a.last} launches of the kernels named "
+             f"*{a.kernel}*.", "",
+             f"{'run':<28}" + "".join(f"{c:>22}" for c in counters)]
+    for lab, d in zip(labels, dirs):
+        db = find_db(d)
+        vals = []
+        for c in counters:
+            v = _per_dispatch(db, c, a.kernel, a.last)
+            vals.append(sum(x for x, _ in v) / len(v) if v else float("nan"))
+        lines.append(f"{lab:<28}" + "".join(f"{x:>22.0f}" for x in vals))
+    if a.note:
+        lines += ["", a.note]
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text, end="")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sp = ap.add_subparsers(dest="cmd_name", required=True)
@@ -401,6 +427,16 @@ def main():
     t.add_argument("--by-grid", action="store_true",
                    help="one row per (kernel, grid) instead of per kernel")
     t.add_argument("--out", required=True)
+    pm = sp.add_parser("pmc")
+    pm.add_argument("--dirs", required=True, help="comma-separated rocprofv3 output directories")
+    pm.add_argument("--labels", required=True)
+    pm.add_argument("--counters", required=True)
+    pm.add_argument("--kernel", required=True, help="substring of the kernel name")
+    pm.add_argument("--last", type=int, default=2)
+    pm.add_argument("--title", required=True)
+    pm.add_argument("--cmd", required=True)
+    pm.add_argument("--note", default="")
+    pm.add_argument("--out", required=True)
     r = sp.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         r.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -410,7 +446,7 @@ def main():
     r.add_argument("--out-txt", required=True)
     a = ap.parse_args()
     {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "launch": cmd_launch,
-     "counters": cmd_counters}[a.cmd_name](a)
+     "counters": cmd_counters, "pmc": cmd_pmc}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
