@@ -170,7 +170,9 @@ def cmd_traffic(a):
 # launch computes: ("flops", n) or ("bytes", n) filled in by launch())
 WORKLOADS = ["gqa_causal_s8192", "mha_causal_s2048", "blockskip_s32768",
              "blockskip_s32768_stress", "chunked_prefill_paged", "paged_decode_gqa",
-             "paged_decode_gqa_mfma", "paged_decode_gqa_fp8", "paged_decode_blockskip_stress"]
+             "paged_decode_gqa_mfma", "paged_decode_gqa_fp8", "paged_decode_shared_prefix",
+             "paged_decode_blockskip", "paged_decode_blockskip_stress",
+             "paged_decode_blockskip_stress_rowmajor"]
 KERNEL_OF = {
     "gqa_causal_s8192": "prefill_bf16_kernel<128, true, false, false>",
     "mha_causal_s2048": "prefill_bf16_kernel<128, true, false, false>",
@@ -180,7 +182,10 @@ KERNEL_OF = {
     "paged_decode_gqa": "decode_split_kernel<128>",
     "paged_decode_gqa_mfma": "decode_native_kernel<128>",
     "paged_decode_gqa_fp8": "decode_fp8_kernel<128, 2>",
+    "paged_decode_shared_prefix": "decode_native_kernel<128>",
+    "paged_decode_blockskip": "decode_skip_kernel<128>",
     "paged_decode_blockskip_stress": "decode_skip_kernel<128>",
+    "paged_decode_blockskip_stress_rowmajor": "decode_skip_rm_kernel<128>",
 }
 SOURCE_OF = {k: ("decode_paged.hip" if k.startswith("paged") else "prefill_bf16.hip")
              for k in WORKLOADS}
@@ -193,7 +198,8 @@ def workload_runner(name: str):
     import torch
     import attention_flash_attn_fwd_amd as A
     from workloads import (CONFIGS, blockskip_inputs, decode_inputs, fp8_decode_inputs,
-                           paged_prefill_inputs, prefill_flops, prefill_inputs)
+                           paged_prefill_inputs, prefill_flops, prefill_inputs,
+                           shared_prefix_decode_inputs)
     dev = "cuda"
     if name in ("gqa_causal_s8192", "mha_causal_s2048"):
         c = CONFIGS[name]
@@ -231,9 +237,28 @@ def workload_runner(name: str):
                                              wc.max_seqlen_q, wc.scale),
                 {"flops": 4 * 32 * 128 * pairs})
     c = CONFIGS["paged_decode_gqa"]
-    layout = "mfma" if name in ("paged_decode_gqa_mfma", "paged_decode_blockskip_stress") \
-        else "rowmajor"
-    amp = 12.0 if name == "paged_decode_blockskip_stress" else 0.0
+    if name == "paged_decode_shared_prefix":
+        # 16 prompts of 1536 tokens, 4 samples each with U[1, 2048] own tokens
+        ds = shared_prefix_decode_inputs(16, 4, c["Hq"], c["Hkv"], c["D"], seed=2004,
+                                         prefix_len=1536, suffix_min=1, suffix_max=2048,
+                                         layout="mfma")[0]
+        sq, sbt, ssl = ds.q.to(dev), ds.block_table.to(dev), ds.seq_lens.to(dev)
+        spools = [(ds.k_pool.to(dev), ds.v_pool.to(dev)) for _ in range(2)]
+        sws = torch.empty(A.attn_decode_workspace_bytes(ds.N, c["Hq"], c["D"], ds.max_blocks,
+                                                        16), dtype=torch.uint8, device=dev)
+        so = torch.empty_like(sq)
+        slse = torch.empty((ds.N, c["Hq"]), dtype=torch.float32, device=dev)
+        sctr = [0]
+
+        def run_shared():
+            kp, vp = spools[sctr[0] % 2]
+            sctr[0] += 1
+            A.attn_decode_paged(sq, kp, vp, sbt, ssl, 16, so, slse, ds.scale, sws, layout="mfma")
+        return run_shared, {"kv_bytes": ds.kv_bytes()}
+    layout = "rowmajor" if name in ("paged_decode_gqa", "paged_decode_gqa_fp8",
+                                    "paged_decode_blockskip_stress_rowmajor") else "mfma"
+    skip = name.startswith("paged_decode_blockskip")
+    amp = 12.0 if "stress" in name else 0.0
     d = decode_inputs(c["N"], c["Hq"], c["Hkv"], c["D"], seed=c["seed"], lmin=c["lmin"],
                       lmax=c["lmax"], layout=layout, sink_amplitude=amp,
                       sink_frac=1 / 64 if amp else 0.0)
@@ -262,7 +287,7 @@ def workload_runner(name: str):
     def run_dec():
         kp, vp = pools[ctr[0] % 2]
         ctr[0] += 1
-        if amp:
+        if skip:
             A.attn_decode_paged_blockskip(q, kp, vp, bt, sl, 16, o, lse, d.scale, 1e-3, ws,
                                           None, None, layout=layout)
         else:
@@ -323,7 +348,7 @@ def cmd_counters(a):
              "share of SIMD cycles the matrix cores worked,",
              "at the clock the chip ran (GRBM_GUI_ACTIVE per XCD / kernel time of the same "
              "dispatch); MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / kernel time.", "",
-             f"{'workload':<30} {'trace us':>9} {'fetch MB':>9} {'write MB':>9} "
+             f"{'workload':<38} {'trace us':>9} {'fetch MB':>9} {'write MB':>9} "
              f"{'MFMA busy':>9} {'clock GHz':>9} {'MFMA TF/s':>9}"]
     for wl in WORKLOADS:
         d = os.path.join(a.dir, wl)
@@ -364,7 +389,7 @@ def cmd_counters(a):
 
         def f(x, k=1.0, nd=1):
             return f"{x / k:>9.{nd}f}" if isinstance(x, (int, float)) else f"{'-':>9}"
-        lines.append(f"{wl:<30} {f(us, 1, 1)} {f(r.get('fetch_bytes'), 1e6)} "
+        lines.append(f"{wl:<38} {f(us, 1, 1)} {f(r.get('fetch_bytes'), 1e6)} "
                      f"{f(r.get('write_bytes'), 1e6)} {f(r.get('mfma_busy_frac'), 0.01)}% "
                      f"{f(r.get('clock_ghz'), 1, 3)} {f(r.get('mfma_tflops'), 1, 1)}")
     with open(a.out_json, "w") as fh:

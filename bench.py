@@ -266,6 +266,7 @@ def main():
         secondary["paged_decode_shared_prefix"] = {
             "logical_kv_GBps": round(logical / ms / 1e9, 1), "us_per_launch": round(ms * 1e6, 2),
             "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "traffic": traffic_of("paged_decode_shared_prefix"),
             "note": "16 prompts x 4 samples, 1536-token shared prompt, U[1,2048] own tokens"}
         del spools
 
@@ -309,8 +310,11 @@ def main():
                 "speedup_vs_dense": round(md / mk, 3),
                 "logical_kv_GBps": round(kvb / mk / 1e9, 1),
                 "read_kv_GBps": round(kvb * (1 - 0.5 * frac) / mk / 1e9, 1), "pool_layout": lay}
-            if amp and lay == "mfma":
-                secondary[label]["traffic"] = traffic_of("paged_decode_blockskip_stress")
+            secondary[label]["traffic"] = traffic_of(
+                {"paged_decode_blockskip": "paged_decode_blockskip",
+                 "paged_decode_blockskip_stress_sinks": "paged_decode_blockskip_stress",
+                 "paged_decode_blockskip_stress_sinks_rowmajor":
+                     "paged_decode_blockskip_stress_rowmajor"}[label])
             del bpools
 
         # chunked prefill over the paged cache: 8 sequences with 3584 cached
